@@ -1,0 +1,259 @@
+"""Pins of the oracle forward: printed sizes, brute force on tiny shapes, closed forms, invariants."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from axial_band_split_amd import synth
+from oracle import brute
+from oracle import model as M
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(**kw):
+    base = dict(sample_rate=44100, n_fft=32, audio_channels=2, num_bands=3, dim=8, depth=1, heads=2, dim_head=4,
+                ff_mult=2, mask_hidden_mult=2, mask_depth=2)
+    base.update(kw)
+    return M.CoreConfig(**base)
+
+
+# ----------------------------------------------------------------------------- printed sizes
+
+def test_param_counts_match_printed():
+    g = json.load(open(os.path.join(GOLDEN, "model_sizes.json")))
+    v, d = g["vocals"], g["deux"]
+    cv = M.CoreConfig(44100, 2048, 2, 60, v["dim"], v["depth"], v["heads"], v["dim_head"], num_stems=v["num_stems"])
+    cd = M.CoreConfig(44100, 2048, 2, 60, d["dim"], d["depth"], d["heads"], d["dim_head"], num_stems=d["num_stems"])
+    assert M.param_count(cv) == v["params"]
+    assert M.param_count(cd) == d["params"]
+    mask_d = sum(int(np.prod(s)) for n, s, _ in M.inventory(cd) if n.startswith("stem"))
+    assert mask_d == d["mask_head_params"]
+    inv = {n: s for n, s, _ in M.inventory(cv)}
+    assert list(inv["stem0.band0.mlp0.weight"]) == v["mask_layer_shapes"][0]
+    assert list(inv["stem0.band0.mlp1.weight"]) == v["mask_layer_shapes"][1]
+    assert list(inv["stem0.band0.mlp2.weight"]) == v["mask_last_layer_band0"]
+    assert list(inv["stem0.band59.mlp2.weight"]) == v["mask_last_layer_band59"]
+    trunk = sum(int(np.prod(s)) for n, s, _ in M.inventory(cv) if n.startswith("layer"))
+    mask = sum(int(np.prod(s)) for n, s, _ in M.inventory(cv) if n.startswith("stem"))
+    assert round(trunk / 1e6, 1) == v["trunk_params_millions"]
+    assert round(mask / 1e6) == v["mask_head_params_millions"]
+
+
+# ----------------------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("kw,B,T,seed", [
+    (dict(), 2, 3, 0),
+    (dict(depth=2), 1, 4, 1),
+    (dict(num_bands=4, n_fft=64, heads=1, dim_head=8, mask_depth=1), 1, 3, 2),
+    (dict(dim=6, heads=3, dim_head=2, mask_depth=3), 2, 2, 3),
+])
+def test_vectorised_matches_brute_force(kw, B, T, seed):
+    cfg = tiny(**kw)
+    ws = synth.draw_weights(M.inventory(cfg), synth.F32, seed=seed, std=0.4, gamma_std=0.3)
+    x = np.random.default_rng(seed + 10).standard_normal((B, (cfg.n_fft // 2 + 1) * 2, T, 2))
+    y = M.forward(x, cfg, ws)
+    yb = np.array(brute.forward(x, cfg.sample_rate, cfg.n_fft, 2, cfg.num_bands, cfg.dim, cfg.depth, cfg.heads,
+                                cfg.dim_head, cfg.mask_depth, M.named(cfg, ws)))
+    assert np.abs(y - yb).max() <= 1e-12 * max(1.0, np.abs(yb).max())
+
+
+def test_brute_force_catches_a_planted_mistake():
+    """A mistake planted in the oracle (a transposed projection) must fail the comparison."""
+    cfg = tiny()
+    ws = synth.draw_weights(M.inventory(cfg), synth.F32, seed=5, std=0.4, gamma_std=0.3)
+    x = np.random.default_rng(7).standard_normal((1, 34, 3, 2))
+    w = M.named(cfg, ws)
+    yb = np.array(brute.forward(x, 44100, 32, 2, 3, 8, 1, 2, 4, 2, w))
+    bad = list(ws)
+    names = [n for n, _, _ in M.inventory(cfg)]
+    i = names.index("layer0.time.attn.to_out.weight")
+    bad[i] = ws[i].T.copy()                     # D == I here, so shapes still agree
+    y = M.forward(x, cfg, bad)
+    assert np.abs(y - yb).max() > 1e-6
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 7))
+    y = M.rmsnorm(x, np.ones(7))
+    assert np.allclose(np.linalg.norm(y, axis=-1), math.sqrt(7), rtol=1e-14)
+    assert np.allclose(M.rmsnorm(3.5 * x, np.ones(7)), y, rtol=1e-14)
+    assert np.all(M.rmsnorm(np.zeros((2, 7)), np.ones(7)) == 0.0)        # the 1e-12 clamp: no NaN
+    g = rng.standard_normal(7)
+    assert np.allclose(M.rmsnorm(x, g), y * g, rtol=1e-14)
+
+
+def test_gelu_and_sigmoid_closed_forms():
+    pts = np.array([-6.0, -2.5, -1.0, -1e-3, 0.0, 0.3, 1.0, 2.0, 7.0])
+    ref = np.array([0.5 * a * (1 + math.erf(a / math.sqrt(2))) for a in pts])
+    assert np.allclose(M.gelu(pts), ref, rtol=1e-15, atol=1e-300)
+    assert np.allclose(M.gelu(pts) - M.gelu(-pts), pts, atol=1e-15)
+    assert M.sigmoid(np.array(0.0)) == 0.5
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(1)
+    n, dh = 11, 8
+    ang = M.rope_angles(n, dh)
+    q = rng.standard_normal((n, dh))
+    k = rng.standard_normal((n, dh))
+    rq, rk = M.rope(q, ang), M.rope(k, ang)
+    assert np.allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-14)
+    assert np.allclose(rq[0], q[0], rtol=0, atol=0)                    # position 0 is the identity
+    # relative position: <R_m a, R_n b> depends only on m - n
+    a, b = q[0], k[0]
+    same_a, same_b = np.tile(a, (n, 1)), np.tile(b, (n, 1))
+    Ra, Rb = M.rope(same_a, ang), M.rope(same_b, ang)
+    d1 = Ra[5] @ Rb[2]
+    d2 = Ra[9] @ Rb[6]
+    assert d1 == pytest.approx(d2, rel=1e-12)
+    # pairs are interleaved (2j, 2j+1): rotating pair j by its angle
+    j, pos = 2, 3
+    th = pos * 10000.0 ** (-2 * j / dh)
+    assert rq[pos, 2 * j] == pytest.approx(q[pos, 2 * j] * math.cos(th) - q[pos, 2 * j + 1] * math.sin(th), rel=1e-13)
+
+
+def test_rope_halves_permutation_leaves_scores_unchanged():
+    """Reordering q's and k's features from interleaved pairs to halves, the same way on
+    both, leaves q . k unchanged (the rewrite the WebGPU export uses)."""
+    rng = np.random.default_rng(2)
+    n, dh = 6, 8
+    ang = M.rope_angles(n, dh)
+    q, k = M.rope(rng.standard_normal((n, dh)), ang), M.rope(rng.standard_normal((n, dh)), ang)
+    perm = np.concatenate([np.arange(0, dh, 2), np.arange(1, dh, 2)])
+    assert np.allclose(q[:, perm] @ k[:, perm].T, q @ k.T, rtol=1e-13)
+
+
+def _attn_weights(cfg, rng, qk_zero=False):
+    D, I, H = cfg.dim, cfg.inner, cfg.heads
+    w = {"p.attn.norm.gamma": np.ones(D),
+         "p.attn.to_qkv.weight": rng.standard_normal((3 * I, D)) * 0.5,
+         "p.attn.to_gates.weight": np.zeros((H, D)),
+         "p.attn.to_gates.bias": np.full(H, 60.0),                 # sigmoid = 1 to double precision
+         "p.attn.to_out.weight": np.eye(D, I)}
+    if qk_zero:
+        w["p.attn.to_qkv.weight"][:2 * I] = 0.0
+    return w
+
+
+def test_attention_special_cases():
+    cfg = tiny(dim=8, heads=2, dim_head=4)
+    rng = np.random.default_rng(3)
+    w = _attn_weights(cfg, rng)
+    # one position: softmax over one key is 1, so the output is v itself
+    x1 = rng.standard_normal((3, 1, 8))
+    v1 = M.rmsnorm(x1, np.ones(8)) @ w["p.attn.to_qkv.weight"][16:24].T
+    assert np.allclose(M.attention(x1, cfg, w, "p."), v1, rtol=1e-13)
+    # zero queries and keys: uniform attention, the output is the mean of v over positions
+    w0 = _attn_weights(cfg, rng, qk_zero=True)
+    x = rng.standard_normal((2, 5, 8))
+    v = M.rmsnorm(x, np.ones(8)) @ w0["p.attn.to_qkv.weight"][16:24].T
+    out = M.attention(x, cfg, w0, "p.")
+    assert np.allclose(out, np.repeat(v.mean(axis=1, keepdims=True), 5, axis=1), rtol=1e-13)
+
+
+def test_softmax_rows_sum_to_one():
+    s = np.random.default_rng(4).standard_normal((3, 7, 9)) * 30
+    p = M.softmax(s)
+    assert np.allclose(p.sum(-1), 1.0, rtol=1e-14) and p.min() >= 0
+
+
+def test_query_blocked_attention_is_exact():
+    """Splitting the sequences into chunks changes nothing (each row normalises alone)."""
+    cfg = tiny(dim=8, heads=2, dim_head=4)
+    rng = np.random.default_rng(5)
+    w = _attn_weights(cfg, rng)
+    w["p.attn.to_gates.weight"] = rng.standard_normal((2, 8))
+    w["p.attn.to_gates.bias"] = rng.standard_normal(2)
+    x = rng.standard_normal((7, 6, 8))
+    assert np.allclose(M.attention(x, cfg, w, "p.", chunk=2), M.attention(x, cfg, w, "p."), rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- whole-core invariants
+
+def _c0_like(**kw):
+    base = dict(sample_rate=44100, n_fft=256, audio_channels=2, num_bands=8, dim=16, depth=1, heads=2, dim_head=8)
+    base.update(kw)
+    return M.CoreConfig(**base)
+
+
+def test_core_is_scale_invariant():
+    """Every band's input is normalised first, so scaling the spectrum changes nothing."""
+    cfg = _c0_like()
+    ws = synth.draw_weights(M.inventory(cfg), synth.F32, seed=1, std=0.2)
+    x = np.random.default_rng(2).standard_normal((1, 258, 5, 2))
+    assert np.allclose(M.forward(7.25 * x, cfg, ws), M.forward(x, cfg, ws), rtol=1e-11, atol=1e-13)
+
+
+def test_constant_band_masks_average_to_the_constant():
+    """Last mask layer zero, value bias c, gate bias 0: every band's mask is c * sigmoid(0) = c/2,
+    so every averaged bin is c/2 whatever the band count."""
+    cfg = _c0_like()
+    inv = M.inventory(cfg)
+    ws = synth.draw_weights(inv, synth.F32, seed=3, std=0.2)
+    c = 0.734
+    for idx, (name, shape, _) in enumerate(inv):
+        if name.startswith("stem0.") and name.endswith(f"mlp{cfg.mask_depth}.weight"):
+            ws[idx] = np.zeros(shape)
+        if name.startswith("stem0.") and name.endswith(f"mlp{cfg.mask_depth}.bias"):
+            W = shape[0] // 2
+            ws[idx] = np.concatenate([np.full(W, c), np.zeros(W)])
+    x = np.random.default_rng(4).standard_normal((2, 258, 3, 2))
+    y = M.forward(x, cfg, ws)
+    assert np.allclose(y, c / 2, rtol=0, atol=1e-15)
+
+
+def test_average_equals_dense_incidence_form():
+    """The index-based scatter average equals (incidence^T m) / counts built densely."""
+    cfg = _c0_like()
+    t = cfg.tables()
+    rng = np.random.default_rng(6)
+    B, T = 2, 4
+    masks = [rng.standard_normal((B, T, W)) for W in t.widths.tolist()]
+    got = M.average(masks, t)
+    S = 2
+    FS = t.n_freqs * S
+    total = t.total_width
+    # dense [FS*2, total] matrix that places each band feature at its (pair, re/im) column
+    P = np.zeros((FS * 2, total))
+    off = 0
+    for i, pairs in enumerate(t.pairs):
+        for r, p in enumerate(pairs.tolist()):
+            for ci in range(2):
+                P[p * 2 + ci, off + r * 2 + ci] = 1.0
+        off += t.widths[i]
+    cnt = P.sum(axis=1)
+    flat = np.concatenate(masks, axis=-1)                    # [B, T, total]
+    dense = (flat @ P.T) / cnt                               # [B, T, FS*2]
+    want = dense.reshape(B, T, FS, 2).transpose(0, 2, 1, 3)
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-15)
+    assert np.array_equal(cnt.reshape(-1, 2)[:, 0], np.repeat(t.counts, S))
+
+
+def test_io_layouts_are_the_printed_planes():
+    """Layout 1 is [B, S*2, F, T] with planes L re, L im, R re, R im."""
+    rng = np.random.default_rng(8)
+    B, F, T, S = 1, 5, 3, 2
+    planes = rng.standard_normal((B, S * 2, F, T))
+    canon = M.read_input(planes, S, 1)
+    for s in range(S):
+        for c in range(2):
+            for f in range(F):
+                for t in range(T):
+                    assert canon[0, f * S + s, t, c] == planes[0, s * 2 + c, f, t]
+    assert np.array_equal(M.write_output(canon, S, 1), planes)
+    assert np.array_equal(synth.fs_t_c_to_sc_f_t(canon, S), planes)
+
+
+def test_c0_forward_runs_in_seconds_and_is_finite():
+    w = synth.WORKLOADS["c0_tiny_fp32"]
+    cfg = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads, w.dim_head)
+    ws = synth.draw_weights(M.inventory(cfg), w.dtype, seed=w.weight_seed)
+    x = synth.draw_input(w)
+    y = M.forward(x, cfg, ws)
+    assert y.shape == (1, 258, 32, 2) and np.isfinite(y).all()
