@@ -1,0 +1,228 @@
+// Memory-bound passes of the core: row norms of the residual stream, the band gather with its
+// per-band normalisation, and the inverse-index mask average.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mbr {
+
+namespace {
+
+// ---------------------------------------------------------------------------------- row norm
+// RMSNorm of the pages ([P1] the RMSNorm paragraph under BandSplit): x / max(||x||, 1e-12) times
+// sqrt(d) times gamma.  One wave per row; lane l holds elements l, l+64, ...  The gains of the
+// norms that feed a projection are folded into that projection's weights, so the pre-projection
+// output here is x * sqrt(D) / max(||x||, eps); the Transformer's output norm applies its gain.
+// Gates of the attention ([P1] "Per Attention layer": to_gates on the normalised input, sigmoid,
+// one per head) are computed from the same fp32 normalised row.
+template <typename T, int NPL>
+__global__ __launch_bounds__(256) void norm_kernel(NormLaunch L) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= L.rows) return;
+  const int D = L.D;
+  float* x = L.x + (size_t)row * D;
+  float v[NPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    v[j] = x[lane + 64 * j];
+    ss += v[j] * v[j];
+  }
+  ss = wave_sum(ss);
+  const float sqrtD = sqrtf((float)D);
+  if (L.mode != 0) {
+    const float inv = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+    ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      v[j] = v[j] * inv * L.gain[lane + 64 * j];
+      x[lane + 64 * j] = v[j];
+      ss += v[j] * v[j];
+    }
+    ss = wave_sum(ss);
+  }
+  T* xh = (T*)L.xh + (size_t)row * D;
+  if (L.mode == 2) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) xh[lane + 64 * j] = cvt<T>(v[j]);
+    return;
+  }
+  const float k = sqrtD / fmaxf(sqrtf(ss), kNormEps);
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    v[j] *= k;
+    xh[lane + 64 * j] = cvt<T>(v[j]);
+  }
+  if (L.gates) {
+    for (int h = 0; h < L.H; ++h) {
+      const float* w = L.wg + (size_t)h * D;
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) a += v[j] * w[lane + 64 * j];
+      a = wave_sum(a);
+      if (lane == 0) L.gates[(size_t)row * L.H + h] = sigmoidf_(a + L.bg[h]);
+    }
+  }
+}
+
+template <typename T>
+hipError_t norm_t(const NormLaunch& L, hipStream_t stream) {
+  dim3 grid((L.rows + 3) / 4), block(256);
+  switch (L.D / 64) {
+    case 1: hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((norm_kernel<T, 3>), grid, block, 0, stream, L); break;
+    case 4: hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, stream, L); break;
+    case 5: hipLaunchKernelGGL((norm_kernel<T, 5>), grid, block, 0, stream, L); break;
+    case 6: hipLaunchKernelGGL((norm_kernel<T, 6>), grid, block, 0, stream, L); break;
+    case 7: hipLaunchKernelGGL((norm_kernel<T, 7>), grid, block, 0, stream, L); break;
+    case 8: hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, stream, L); break;
+    case 9: hipLaunchKernelGGL((norm_kernel<T, 9>), grid, block, 0, stream, L); break;
+    case 10: hipLaunchKernelGGL((norm_kernel<T, 10>), grid, block, 0, stream, L); break;
+    case 11: hipLaunchKernelGGL((norm_kernel<T, 11>), grid, block, 0, stream, L); break;
+    case 12: hipLaunchKernelGGL((norm_kernel<T, 12>), grid, block, 0, stream, L); break;
+    case 13: hipLaunchKernelGGL((norm_kernel<T, 13>), grid, block, 0, stream, L); break;
+    case 14: hipLaunchKernelGGL((norm_kernel<T, 14>), grid, block, 0, stream, L); break;
+    case 15: hipLaunchKernelGGL((norm_kernel<T, 15>), grid, block, 0, stream, L); break;
+    case 16: hipLaunchKernelGGL((norm_kernel<T, 16>), grid, block, 0, stream, L); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------- band gather
+// [P1] "The forward chain" and "The mel-band split, exactly": each band takes its (bin, channel)
+// pairs in order, real and imaginary part as neighbouring features, and is normalised over its own
+// features (the gain and sqrt(W_i) are folded into the band's projection).  Workgroup per
+// (64 frames, batch, band); lanes run along frames so every input load is coalesced; the band's
+// rows are assembled in LDS and written out as one contiguous block of U.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(GatherLaunch L) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  T* tile = (T*)lds_raw;                       // [64][kpad]
+  __shared__ float part[4][64];
+  __shared__ float scale[64];
+  const int band = blockIdx.z, b = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
+  const int t = t0 + lane;
+  const bool valid = t < L.frames;
+  const int foff = L.band_info[band * 4 + 0], width = L.band_info[band * 4 + 1];
+  const int kpad = L.band_info[band * 4 + 2], ucol = L.band_info[band * 4 + 3];
+  const int npairs = width / 2;
+  const int* pairs = L.gather_pair + foff / 2;
+  const int F = L.n_freqs, S = L.channels, FS = F * S, T_ = L.frames;
+  auto load = [&](int p, float& re, float& im) {
+    if (!valid) { re = im = 0.f; return; }
+    if (L.layout == 0) {
+      const float2 z = *(const float2*)(L.in + (((size_t)b * FS + p) * T_ + t) * 2);
+      re = z.x; im = z.y;
+    } else {
+      const int f = p / S, s = p - f * S;
+      const float* base = L.in + ((size_t)b * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + t;
+      re = base[0];
+      im = base[(size_t)F * T_];
+    }
+  };
+  float ss = 0.f;
+  for (int j = wq; j < npairs; j += 4) {
+    float re, im;
+    load(pairs[j], re, im);
+    ss += re * re + im * im;
+  }
+  part[wq][lane] = ss;
+  __syncthreads();
+  if (wq == 0) {
+    const float tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    scale[lane] = 1.0f / fmaxf(sqrtf(tot), kNormEps);
+  }
+  __syncthreads();
+  const float sc = scale[lane];
+  for (int j = wq; j < npairs; j += 4) {
+    float re, im;
+    load(pairs[j], re, im);
+    tile[lane * kpad + 2 * j] = cvt<T>(re * sc);
+    tile[lane * kpad + 2 * j + 1] = cvt<T>(im * sc);
+  }
+  for (int e = width + wq; e < kpad; e += 4) tile[lane * kpad + e] = cvt<T>(0.f);
+  __syncthreads();
+  // rows b*T + t0 .. of band `band`: contiguous in U at column block ucol
+  const int rows = min(64, T_ - t0);
+  const size_t BT = (size_t)L.batch * T_;
+  T* dst = (T*)L.U + (size_t)ucol * BT + ((size_t)b * T_ + t0) * kpad;
+  const int n16 = rows * kpad * (int)sizeof(T) / 16;
+  for (int c = threadIdx.x; c < n16; c += 256) ((uint4*)dst)[c] = ((const uint4*)tile)[c];
+}
+
+// ---------------------------------------------------------------------------------- average
+// [P1] "The forward chain": the band masks go back to their (bin, channel) pairs and each value
+// is divided by the number of bands covering its bin.  Instead of a scatter with atomics, every
+// output element reads its (at most two) sources through the inverse index and multiplies by the
+// precomputed 1/count: deterministic, one write per element.  Threads run along frames.
+__global__ __launch_bounds__(256) void average_kernel(AverageLaunch L) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int p = blockIdx.y;                   // pair f*S + s
+  const int bs = blockIdx.z;                  // b * stems + stem
+  if (t >= L.frames) return;
+  const int T_ = L.frames, S = L.channels, F = L.n_freqs;
+  const int b = bs / L.stems, st = bs - b * L.stems;
+  const int s1 = L.inv_slot[2 * p], s2 = L.inv_slot[2 * p + 1];
+  const float w = L.inv_weight[p];
+  const float* M = L.M + ((size_t)st * L.batch + b) * (size_t)L.total * T_;
+  float re = M[(size_t)(2 * s1) * T_ + t], im = M[(size_t)(2 * s1 + 1) * T_ + t];
+  if (s2 >= 0) {
+    re += M[(size_t)(2 * s2) * T_ + t];
+    im += M[(size_t)(2 * s2 + 1) * T_ + t];
+  }
+  re *= w;
+  im *= w;
+  if (L.layout == 0) {
+    *(float2*)(L.out + (((size_t)bs * F * S + p) * T_ + t) * 2) = make_float2(re, im);
+  } else {
+    const int f = p / S, s = p - f * S;
+    float* base = L.out + ((size_t)bs * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + t;
+    base[0] = re;
+    base[(size_t)F * T_] = im;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_norm(const NormLaunch& L, hipStream_t stream) {
+  if (L.rows <= 0) return hipSuccess;
+  if (L.D % 64 || L.D > 1024) return hipErrorInvalidValue;
+  switch (L.dtype) {
+    case DT_F32: return norm_t<float>(L, stream);
+    case DT_F16: return norm_t<f16>(L, stream);
+    case DT_BF16: return norm_t<bf16>(L, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t gather_t(const GatherLaunch& L, hipStream_t stream) {
+  dim3 grid((L.frames + 63) / 64, L.batch, L.num_bands), block(256);
+  const size_t lds = (size_t)64 * L.max_kpad * sizeof(T);
+  if (lds > 160 * 1024 - 2048) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)gather_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gather_kernel<T>, grid, block, lds, stream, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherLaunch& L, hipStream_t stream) {
+  switch (L.dtype) {
+    case DT_F32: return gather_t<float>(L, stream);
+    case DT_F16: return gather_t<f16>(L, stream);
+    case DT_BF16: return gather_t<bf16>(L, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_average(const AverageLaunch& L, hipStream_t stream) {
+  dim3 grid((L.frames + 255) / 256, L.n_freqs * L.channels, L.batch * L.stems), block(256);
+  hipLaunchKernelGGL(average_kernel, grid, block, 0, stream, L);
+  return hipGetLastError();
+}
+
+}  // namespace mbr

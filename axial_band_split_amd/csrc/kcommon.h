@@ -1,0 +1,57 @@
+// Device-side types shared by the kernels of the core: element types, 16-byte MFMA operand
+// fragments, the gfx950 matrix-core instructions used, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mbr {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Each lane feeds 16 bytes of A and 16 bytes of B per matrix-core step:
+//   f16 / bf16: v_mfma_f32_16x16x32 (8 elements per lane, K = 32 per step)
+//   f32:        4 x v_mfma_f32_16x16x4f32 (4 elements per lane, K = 16 per step)
+// Lane l holds row (A) / column (B) l % 16 and K elements EPF*(l/16) .. EPF*(l/16)+EPF-1.  The
+// accumulator C (16x16) holds, in lane l, column l % 16 and rows 4*(l/16) .. 4*(l/16)+3.
+template <typename T> struct Frag;
+template <> struct Frag<f16> { typedef f16x8 type; typedef f16x4 half_type; static constexpr int EPF = 8; };
+template <> struct Frag<bf16> { typedef bf16x8 type; typedef bf16x4 half_type; static constexpr int EPF = 8; };
+template <> struct Frag<float> { typedef f32x4 type; typedef float half_type; static constexpr int EPF = 4; };
+
+__device__ __forceinline__ void mma(f32x4& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32: the four instructions take the lane's elements 0..3 in turn; lane group g = l/16 is the
+// instruction's own k index, so instruction j covers k = 4*g + j of the 16 and all four together
+// cover every k once (the k order of a sum is free).
+__device__ __forceinline__ void mma(f32x4& c, const f32x4& a, const f32x4& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T cvt(float x) { return (T)x; }
+template <typename T> __device__ __forceinline__ float tof(T x) { return (float)x; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+constexpr float kNormEps = 1e-12f;
+
+}  // namespace mbr

@@ -1,0 +1,124 @@
+// Launchers of the core's HIP kernels (host side) and the descriptors they share with the
+// library.  Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mbr {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// One problem of a grouped GEMM  C = A . B^T  (A [M, K] row-major, B [N, K] row-major: the
+// weights in their [out, in] form).  Offsets are in elements; the parts marked "b" are multiplied
+// by the forward's rows per group (batch * frames) at run time, so one descriptor serves every
+// batch size.
+struct GemmGroup {
+  int64_t a_off0, a_offb;   // A element offset = a_off0 + a_offb * rows
+  int64_t b_off;            // B element offset
+  int64_t c_off0, c_offb;   // C element offset (epilogue-specific meaning)
+  int64_t bias_off;         // bias element offset
+  int32_t N, K, lda, ldb;
+  int32_t e0, e1;           // epilogue extras (GLU: feature offset, band width)
+};
+
+struct GemmTile {
+  int32_t group, m0, n0, pad;
+};
+
+// Epilogue kinds of the GEMM family.
+enum Epi {
+  EPI_EMBED = 0,     // C(float) = acc + bias                      (band embedding)
+  EPI_QKV = 1,       // rotary on q, k; scatter q, k, v^T into attention layout
+  EPI_GELU = 2,      // C(T) = gelu(acc + bias)                       (FFN1)
+  EPI_RESID = 3,     // C(float) += acc (+ bias)                      (out-proj, FFN2)
+  EPI_TANH = 4,      // C(T) = tanh(acc + bias)                       (mask MLP hidden layers)
+  EPI_GLU = 5,       // paired value/gate columns -> value*sigmoid(gate), feature-major float
+};
+
+struct QkvArgs {
+  void* q;            // [seqs][H][npad][dh]
+  void* k;            // [seqs][H][npad][dh]
+  void* vt;           // [seqs][H][dh][npad]
+  const float* cos;   // [npos][dh/2]
+  const float* sin;
+  int32_t axis;       // 0: time (seq = row / T, pos = row % T); 1: band (seq = row % (B*T), pos = row / (B*T))
+  int32_t frames, batch, heads, dh, npad;
+};
+
+struct GemmLaunch {
+  int dtype;                    // DT_*
+  int epi;                      // Epi
+  const void* A;
+  const void* B;
+  void* C;
+  const float* bias;
+  int64_t ldc;
+  int32_t M;                    // rows of every group for this launch
+  // dense (single-problem) launch when tiles == nullptr
+  GemmGroup dense;
+  // grouped launch
+  const GemmGroup* groups;      // device array
+  const GemmTile* tiles;        // device array
+  int32_t n_tiles;
+  QkvArgs qkv;
+  // GLU output layout: C[(b)][feature][t] with total features `glu_total`, frames `glu_frames`
+  int32_t glu_total, glu_frames;
+};
+
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t stream);
+
+// Row RMS norm passes over the fp32 residual stream x [rows, D].
+//   mode 0: xh = T(x * sqrt(D) / max(|x|, eps)); gates (optional) from the same normalised row
+//   mode 1: y = x * gain / max(|x|, eps); x = y; then xh, gates as mode 0 applied to y
+//   mode 2: y = x * gain / max(|x|, eps); x = y; xh = T(y)
+struct NormLaunch {
+  int dtype;
+  int mode;
+  float* x;
+  void* xh;
+  const float* gain;       // [D] (gamma * sqrt(D)) for modes 1, 2
+  float* gates;            // [rows, H] or nullptr
+  const float* wg;         // [H, D] gate weights (gamma folded), fp32
+  const float* bg;         // [H]
+  int32_t rows, D, H;
+};
+hipError_t launch_norm(const NormLaunch& L, hipStream_t stream);
+
+// Band gather + per-band L2 normalisation of the complex stereo input into the half/float
+// matrix U: per band i, rows b*T + t, columns = band features (zero padded to kpad_i).
+struct GatherLaunch {
+  int dtype;
+  const float* in;
+  void* U;
+  const int32_t* band_info;   // [NB][4]: feature offset, width, kpad, U column offset (sum of kpad before)
+  const int32_t* gather_pair; // slot -> pair
+  int32_t num_bands, batch, frames, n_freqs, channels, layout, max_kpad;
+};
+hipError_t launch_gather(const GatherLaunch& L, hipStream_t stream);
+
+// Attention over sequences held in [seqs][H][npad][dh] (q, k) and [seqs][H][dh][npad] (v^T);
+// writes O * gate into token layout O[row][H*dh].
+struct AttnLaunch {
+  int dtype;
+  int axis;                 // 0 time (flash, n = T), 1 band (n = NB <= 64, one wave per sequence-head)
+  const void* q;
+  const void* k;
+  const void* vt;
+  const float* gates;       // [rows][H]
+  void* o;                  // [rows][H*dh]
+  int32_t n, npad, seqs, heads, dh, frames, batch;
+  float scale_log2;         // dh^-1/2 * log2(e) when the scale is not folded; 1*log2(e) otherwise
+};
+hipError_t launch_attention(const AttnLaunch& L, hipStream_t stream);
+
+// Inverse-index average of the GLU output M [stems][B][ΣW][T] into the masks.
+struct AverageLaunch {
+  const float* M;
+  float* out;
+  const int32_t* inv_slot;   // [F*S][2]
+  const float* inv_weight;   // [F*S]
+  int32_t batch, stems, total, frames, n_freqs, channels, layout;
+};
+hipError_t launch_average(const AverageLaunch& L, hipStream_t stream);
+
+}  // namespace mbr

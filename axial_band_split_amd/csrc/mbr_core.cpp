@@ -1,0 +1,831 @@
+// C ABI of the Mel-Band RoFormer core: configuration, weight repacking, workspace and the launch
+// sequence of one forward.  The functions declared in include/mbr_core.h live here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mbr_core.h"
+#include "kernels.h"
+#include "tables.h"
+
+using namespace mbr;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(MBR_E_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+size_t dtype_size(int dt) { return dt == MBR_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------------- host numerics
+float bf16_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+uint16_t float_to_bf16(float f) {  // round to nearest even
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+std::vector<double> to_double(const std::vector<char>& raw, int dt, size_t n) {
+  std::vector<double> out(n);
+  if (dt == MBR_F32) {
+    const float* p = (const float*)raw.data();
+    for (size_t i = 0; i < n; ++i) out[i] = p[i];
+  } else if (dt == MBR_F16) {
+    const _Float16* p = (const _Float16*)raw.data();
+    for (size_t i = 0; i < n; ++i) out[i] = (double)(float)p[i];
+  } else {
+    const uint16_t* p = (const uint16_t*)raw.data();
+    for (size_t i = 0; i < n; ++i) out[i] = bf16_to_float(p[i]);
+  }
+  return out;
+}
+
+// Append values (double) in dtype to a byte buffer, 256-byte aligned start; returns element offset.
+struct Packer {
+  int dt;
+  std::vector<char> bytes;
+  size_t append(const std::vector<double>& v) {
+    size_t esz = dtype_size(dt);
+    size_t pos = bytes.size();
+    size_t aligned = (pos + 255) / 256 * 256;
+    bytes.resize(aligned + v.size() * esz);
+    char* p = bytes.data() + aligned;
+    for (size_t i = 0; i < v.size(); ++i) {
+      float f = (float)v[i];
+      if (dt == MBR_F32) {
+        std::memcpy(p + 4 * i, &f, 4);
+      } else if (dt == MBR_F16) {
+        _Float16 h = (_Float16)f;
+        std::memcpy(p + 2 * i, &h, 2);
+      } else {
+        uint16_t b = float_to_bf16(f);
+        std::memcpy(p + 2 * i, &b, 2);
+      }
+    }
+    return aligned / esz;
+  }
+};
+struct FPacker {  // fp32 side tables (biases, gains, gate weights)
+  std::vector<float> v;
+  size_t append(const std::vector<double>& x) {
+    size_t pos = (v.size() + 63) / 64 * 64;
+    v.resize(pos + x.size());
+    for (size_t i = 0; i < x.size(); ++i) v[pos + i] = (float)x[i];
+    return pos;
+  }
+};
+
+struct TransformerW {
+  size_t wqkv, wout, w1, w2;          // element offsets in the dtype weight block
+  size_t wg, bg, b1, b2, gout;        // float offsets
+};
+struct MaskW {
+  std::vector<size_t> w;              // per layer: offset of band 0's matrix (bands contiguous per layer)
+  std::vector<std::vector<size_t>> wband;  // [layer][band] element offsets
+  std::vector<std::vector<size_t>> bband;  // [layer][band] float offsets
+};
+
+}  // namespace
+
+struct mbr_core {
+  mbr_config cfg;
+  Bands bands;
+  int device = 0;
+  int NB = 0, D = 0, H = 0, DH = 0, I = 0, FF = 0, MH = 0, T = 0, Tp = 0, Bmax = 0, total = 0;
+  std::vector<int> kpad, kcol, wp;    // per band: padded K of the embedding, U column block, mask N/2
+  int kpad_total = 0, kpad_max = 0;
+  // device memory
+  char* wdev = nullptr;               // dtype weights
+  float* fdev = nullptr;              // fp32 side tables
+  size_t emb_w = 0, emb_b = 0;
+  std::vector<size_t> emb_wband;
+  std::vector<TransformerW> tw;
+  std::vector<MaskW> mw;              // per stem
+  void* ws = nullptr;                 // workspace block
+  size_t ws_bytes = 0, w_bytes = 0, f_bytes = 0;
+  float* X = nullptr;
+  void* XH = nullptr;
+  float* gates = nullptr;
+  void* U = nullptr;
+  void *qt = nullptr, *kt = nullptr, *vtt = nullptr, *qb = nullptr, *kb = nullptr, *vtb = nullptr;
+  void* O = nullptr;
+  void* H1 = nullptr;
+  void* H2 = nullptr;
+  float* Mglu = nullptr;
+  // tables
+  int32_t* band_info = nullptr;
+  int32_t* gather_pair = nullptr;
+  int32_t* inv_slot = nullptr;
+  float* inv_weight = nullptr;
+  float *cos_t = nullptr, *sin_t = nullptr, *cos_b = nullptr, *sin_b = nullptr;
+  // grouped GEMM descriptors
+  GemmGroup* groups = nullptr;
+  GemmTile* tiles = nullptr;
+  int g_embed = 0, t_embed = 0, n_embed = 0;
+  std::vector<std::vector<int>> g_mask, t_mask, n_mask;  // [stem][layer] group start, tile start, tile count
+  char* tables_dev = nullptr;
+};
+
+namespace {
+
+int check_device(int* dev) {
+  HIP_TRY(hipGetDevice(dev));
+  hipDeviceProp_t p;
+  HIP_TRY(hipGetDeviceProperties(&p, *dev));
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0)
+    return fail(MBR_E_DEVICE, std::string("device is ") + p.gcnArchName + ", this library is built for gfx950");
+  return MBR_OK;
+}
+
+int setup_tables_and_groups(mbr_core* c) {
+  const mbr_config& cfg = c->cfg;
+  const Bands& bd = c->bands;
+  // band info [NB][4]
+  std::vector<int32_t> info(c->NB * 4);
+  for (int i = 0; i < c->NB; ++i) {
+    info[4 * i + 0] = bd.offset[i];
+    info[4 * i + 1] = bd.width[i];
+    info[4 * i + 2] = c->kpad[i];
+    info[4 * i + 3] = c->kcol[i];
+  }
+  std::vector<float> ct, st, cb, sb;
+  rope_tables(c->Tp, c->DH, &ct, &st);
+  rope_tables(64, c->DH, &cb, &sb);
+
+  // grouped GEMM descriptors
+  std::vector<GemmGroup> groups;
+  std::vector<GemmTile> tiles;
+  const int MT = (c->Bmax * c->T + 127) / 128;  // row tiles for the largest batch
+  auto add_tiles = [&](int group, int N) {
+    for (int m = 0; m < MT; ++m)
+      for (int n = 0; n < (N + 127) / 128; ++n) tiles.push_back({group, m * 128, n * 128, 0});
+  };
+  c->g_embed = 0;
+  c->t_embed = 0;
+  for (int i = 0; i < c->NB; ++i) {
+    GemmGroup g{};
+    g.a_off0 = 0;
+    g.a_offb = c->kcol[i];
+    g.b_off = (int64_t)c->emb_wband[i];
+    g.c_off0 = 0;
+    g.c_offb = (int64_t)i * c->D;
+    g.bias_off = (int64_t)c->emb_b + (int64_t)i * c->D;
+    g.N = c->D;
+    g.K = c->kpad[i];
+    g.lda = c->kpad[i];
+    g.ldb = c->kpad[i];
+    groups.push_back(g);
+    add_tiles((int)groups.size() - 1, g.N);
+  }
+  c->n_embed = (int)tiles.size();
+  const int nl = cfg.mask_depth + 1;
+  c->g_mask.assign(cfg.num_stems, std::vector<int>(nl));
+  c->t_mask.assign(cfg.num_stems, std::vector<int>(nl));
+  c->n_mask.assign(cfg.num_stems, std::vector<int>(nl));
+  for (int s = 0; s < cfg.num_stems; ++s) {
+    for (int j = 0; j < nl; ++j) {
+      c->g_mask[s][j] = (int)groups.size();
+      c->t_mask[s][j] = (int)tiles.size();
+      for (int i = 0; i < c->NB; ++i) {
+        GemmGroup g{};
+        const int K = j == 0 ? c->D : c->MH;
+        g.a_off0 = 0;
+        g.a_offb = (int64_t)i * K;
+        g.b_off = (int64_t)c->mw[s].wband[j][i];
+        g.bias_off = (int64_t)c->mw[s].bband[j][i];
+        g.K = K;
+        g.lda = K;
+        g.ldb = K;
+        if (j < nl - 1) {
+          g.N = c->MH;
+          g.c_off0 = 0;
+          g.c_offb = (int64_t)i * c->MH;
+        } else {
+          g.N = 2 * c->wp[i];
+          g.c_off0 = 0;
+          g.c_offb = (int64_t)s * c->total;   // stem block of the GLU output, times rows (B*T)
+          g.e0 = bd.offset[i];
+          g.e1 = bd.width[i];
+        }
+        groups.push_back(g);
+        add_tiles((int)groups.size() - 1, g.N);
+      }
+      c->n_mask[s][j] = (int)tiles.size() - c->t_mask[s][j];
+    }
+  }
+
+  // one device block for all tables
+  size_t off = 0;
+  auto place = [&](size_t bytes) {
+    size_t o = (off + 255) / 256 * 256;
+    off = o + bytes;
+    return o;
+  };
+  size_t o_info = place(info.size() * 4), o_gp = place(bd.gather_pair.size() * 4),
+         o_inv = place(bd.inv_slot.size() * 4), o_w = place(bd.inv_weight.size() * 4), o_ct = place(ct.size() * 4),
+         o_st = place(st.size() * 4), o_cb = place(cb.size() * 4), o_sb = place(sb.size() * 4),
+         o_g = place(groups.size() * sizeof(GemmGroup)), o_t = place(tiles.size() * sizeof(GemmTile));
+  std::vector<char> host(off);
+  std::memcpy(host.data() + o_info, info.data(), info.size() * 4);
+  std::memcpy(host.data() + o_gp, bd.gather_pair.data(), bd.gather_pair.size() * 4);
+  std::memcpy(host.data() + o_inv, bd.inv_slot.data(), bd.inv_slot.size() * 4);
+  std::memcpy(host.data() + o_w, bd.inv_weight.data(), bd.inv_weight.size() * 4);
+  std::memcpy(host.data() + o_ct, ct.data(), ct.size() * 4);
+  std::memcpy(host.data() + o_st, st.data(), st.size() * 4);
+  std::memcpy(host.data() + o_cb, cb.data(), cb.size() * 4);
+  std::memcpy(host.data() + o_sb, sb.data(), sb.size() * 4);
+  std::memcpy(host.data() + o_g, groups.data(), groups.size() * sizeof(GemmGroup));
+  std::memcpy(host.data() + o_t, tiles.data(), tiles.size() * sizeof(GemmTile));
+  HIP_TRY(hipMalloc(&c->tables_dev, off));
+  HIP_TRY(hipMemcpy(c->tables_dev, host.data(), off, hipMemcpyHostToDevice));
+  char* b = c->tables_dev;
+  c->band_info = (int32_t*)(b + o_info);
+  c->gather_pair = (int32_t*)(b + o_gp);
+  c->inv_slot = (int32_t*)(b + o_inv);
+  c->inv_weight = (float*)(b + o_w);
+  c->cos_t = (float*)(b + o_ct);
+  c->sin_t = (float*)(b + o_st);
+  c->cos_b = (float*)(b + o_cb);
+  c->sin_b = (float*)(b + o_sb);
+  c->groups = (GemmGroup*)(b + o_g);
+  c->tiles = (GemmTile*)(b + o_t);
+  return MBR_OK;
+}
+
+int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
+  const mbr_config& cfg = c->cfg;
+  const Bands& bd = c->bands;
+  const int D = c->D, I = c->I, H = c->H, FF = c->FF, MH = c->MH;
+  Packer pk{cfg.dtype, {}};
+  FPacker fp;
+  size_t idx = 0;
+  // band embedding: fold gamma_i * sqrt(W_i) into the projection, pad K to kpad_i
+  c->emb_wband.resize(c->NB);
+  std::vector<double> emb_bias;
+  for (int i = 0; i < c->NB; ++i) {
+    const std::vector<double>& g = W[idx++];
+    const std::vector<double>& A = W[idx++];
+    const std::vector<double>& b = W[idx++];
+    const int Wi = bd.width[i], kp = c->kpad[i];
+    const double r = std::sqrt((double)Wi);
+    std::vector<double> m((size_t)D * kp, 0.0);
+    for (int d = 0; d < D; ++d)
+      for (int e = 0; e < Wi; ++e) m[(size_t)d * kp + e] = A[(size_t)d * Wi + e] * g[e] * r;
+    c->emb_wband[i] = pk.append(m);
+    emb_bias.insert(emb_bias.end(), b.begin(), b.end());
+  }
+  c->emb_b = fp.append(emb_bias);
+  // transformers: attention gain (and the query scale dh^-1/2) folded into W_qkv and the gate
+  // weights; feed-forward gain into W_1; output gain times sqrt(D) kept as a vector
+  const double qscale = 1.0 / std::sqrt((double)c->DH);
+  c->tw.resize(2 * cfg.depth);
+  for (int t = 0; t < 2 * cfg.depth; ++t) {
+    const auto& ga = W[idx++];
+    const auto& wqkv = W[idx++];
+    const auto& wg = W[idx++];
+    const auto& bg = W[idx++];
+    const auto& wout = W[idx++];
+    const auto& gf = W[idx++];
+    const auto& w1 = W[idx++];
+    const auto& b1 = W[idx++];
+    const auto& w2 = W[idx++];
+    const auto& b2 = W[idx++];
+    const auto& go = W[idx++];
+    std::vector<double> q((size_t)3 * I * D);
+    for (int o = 0; o < 3 * I; ++o)
+      for (int e = 0; e < D; ++e) q[(size_t)o * D + e] = wqkv[(size_t)o * D + e] * ga[e] * (o < I ? qscale : 1.0);
+    std::vector<double> g((size_t)H * D);
+    for (int h = 0; h < H; ++h)
+      for (int e = 0; e < D; ++e) g[(size_t)h * D + e] = wg[(size_t)h * D + e] * ga[e];
+    std::vector<double> f1((size_t)FF * D);
+    for (int o = 0; o < FF; ++o)
+      for (int e = 0; e < D; ++e) f1[(size_t)o * D + e] = w1[(size_t)o * D + e] * gf[e];
+    std::vector<double> gout(D);
+    for (int e = 0; e < D; ++e) gout[e] = go[e] * std::sqrt((double)D);
+    TransformerW& tw = c->tw[t];
+    tw.wqkv = pk.append(q);
+    tw.wout = pk.append(wout);
+    tw.w1 = pk.append(f1);
+    tw.w2 = pk.append(w2);
+    tw.wg = fp.append(g);
+    tw.bg = fp.append(bg);
+    tw.b1 = fp.append(b1);
+    tw.b2 = fp.append(b2);
+    tw.gout = fp.append(gout);
+  }
+  // mask head: per stem, per layer, bands in order; the last layer's value and gate rows
+  // interleaved in blocks of 16 features so a GLU pair lands in one lane
+  const int nl = cfg.mask_depth + 1;
+  c->mw.resize(cfg.num_stems);
+  for (int s = 0; s < cfg.num_stems; ++s) {
+    MaskW& m = c->mw[s];
+    m.wband.assign(nl, std::vector<size_t>(c->NB));
+    m.bband.assign(nl, std::vector<size_t>(c->NB));
+    for (int i = 0; i < c->NB; ++i) {
+      for (int j = 0; j < nl; ++j) {
+        const auto& w = W[idx++];
+        const auto& b = W[idx++];
+        if (j < nl - 1) {
+          m.wband[j][i] = pk.append(w);
+          m.bband[j][i] = fp.append(b);
+        } else {
+          const int Wi = bd.width[i], wp = c->wp[i];
+          std::vector<double> r((size_t)2 * wp * MH, 0.0), rb((size_t)2 * wp, 0.0);
+          for (int q = 0; q < wp / 16; ++q)
+            for (int k = 0; k < 16; ++k) {
+              const int e = 16 * q + k;
+              if (e >= Wi) continue;
+              for (int x = 0; x < MH; ++x) {
+                r[(size_t)(32 * q + k) * MH + x] = w[(size_t)e * MH + x];
+                r[(size_t)(32 * q + 16 + k) * MH + x] = w[(size_t)(Wi + e) * MH + x];
+              }
+              rb[32 * q + k] = b[e];
+              rb[32 * q + 16 + k] = b[Wi + e];
+            }
+          m.wband[j][i] = pk.append(r);
+          m.bband[j][i] = fp.append(rb);
+        }
+      }
+    }
+  }
+  c->w_bytes = pk.bytes.size();
+  c->f_bytes = fp.v.size() * 4;
+  HIP_TRY(hipMalloc(&c->wdev, c->w_bytes));
+  HIP_TRY(hipMemcpy(c->wdev, pk.bytes.data(), c->w_bytes, hipMemcpyHostToDevice));
+  HIP_TRY(hipMalloc(&c->fdev, c->f_bytes));
+  HIP_TRY(hipMemcpy(c->fdev, fp.v.data(), c->f_bytes, hipMemcpyHostToDevice));
+  return MBR_OK;
+}
+
+int alloc_workspace(mbr_core* c) {
+  const size_t esz = dtype_size(c->cfg.dtype);
+  const size_t BT = (size_t)c->Bmax * c->T, NT = (size_t)c->NB * BT;
+  size_t off = 0;
+  auto place = [&](size_t bytes) {
+    size_t o = (off + 255) / 256 * 256;
+    off = o + bytes;
+    return o;
+  };
+  const size_t attn_t = (size_t)c->NB * c->Bmax * c->H * c->Tp * c->DH * esz;
+  const size_t attn_b = BT * c->H * 64 * c->DH * esz;
+  size_t oX = place(NT * c->D * 4), oXH = place(NT * c->D * esz), oG = place(NT * c->H * 4),
+         oU = place(BT * c->kpad_total * esz), oqt = place(attn_t), okt = place(attn_t), ovt = place(attn_t),
+         oqb = place(attn_b), okb = place(attn_b), ovb = place(attn_b), oO = place(NT * c->I * esz),
+         oH1 = place(NT * std::max(c->FF, c->MH) * esz), oH2 = place(NT * c->MH * esz),
+         oM = place((size_t)c->cfg.num_stems * BT * c->total * 4);
+  c->ws_bytes = off;
+  hipError_t e = hipMalloc(&c->ws, off);
+  if (e != hipSuccess) return fail(MBR_E_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+  HIP_TRY(hipMemset(c->ws, 0, off));
+  char* b = (char*)c->ws;
+  c->X = (float*)(b + oX);
+  c->XH = b + oXH;
+  c->gates = (float*)(b + oG);
+  c->U = b + oU;
+  c->qt = b + oqt;
+  c->kt = b + okt;
+  c->vtt = b + ovt;
+  c->qb = b + oqb;
+  c->kb = b + okb;
+  c->vtb = b + ovb;
+  c->O = b + oO;
+  c->H1 = b + oH1;
+  c->H2 = b + oH2;
+  c->Mglu = (float*)(b + oM);
+  return MBR_OK;
+}
+
+// ---------------------------------------------------------------------------------- forward
+// Optional per-launch event timing (mbr_core_forward_profiled).
+struct Prof {
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
+  hipStream_t s;
+  int begin(int kind) {
+    hipEvent_t a, b;
+    HIP_TRY(hipEventCreate(&a));
+    HIP_TRY(hipEventCreate(&b));
+    marks.push_back({kind, {a, b}});
+    HIP_TRY(hipEventRecord(a, s));
+    return MBR_OK;
+  }
+  int end() {
+    HIP_TRY(hipEventRecord(marks.back().second.second, s));
+    return MBR_OK;
+  }
+};
+
+#define LAUNCH(kind, expr)                        \
+  do {                                            \
+    if (prof) { int r_ = prof->begin(kind); if (r_) return r_; } \
+    HIP_TRY(expr);                                \
+    if (prof) { int r_ = prof->end(); if (r_) return r_; } \
+  } while (0)
+
+int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t s, int stop_stage,
+                Prof* prof = nullptr) {
+  const mbr_config& cfg = c->cfg;
+  const int dt = cfg.dtype;
+  const int BT = batch * c->T;
+  const int NT = c->NB * BT;
+  const char* W = c->wdev;
+  const size_t esz = dtype_size(dt);
+  auto wptr = [&](size_t off) { return (const void*)(W + off * esz); };
+
+  GatherLaunch gl{dt, in, c->U, c->band_info, c->gather_pair, c->NB, batch, c->T, c->bands.n_freqs,
+                  c->bands.channels, cfg.io_layout, c->kpad_max};
+  LAUNCH(MBR_K_GATHER, launch_gather(gl, s));
+
+  GemmLaunch ge{};
+  ge.dtype = dt;
+  ge.epi = EPI_EMBED;
+  ge.A = c->U;
+  ge.B = W;
+  ge.C = c->X;
+  ge.bias = c->fdev;
+  ge.ldc = c->D;
+  ge.M = BT;
+  ge.groups = c->groups;
+  ge.tiles = c->tiles + c->t_embed;
+  ge.n_tiles = c->n_embed;
+  LAUNCH(MBR_K_EMBED, launch_gemm(ge, s));
+
+  NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
+  LAUNCH(MBR_K_NORM, launch_norm(nl, s));
+  if (stop_stage == 0) return MBR_OK;
+
+  const int ntr = 2 * cfg.depth;
+  for (int t = 0; t < ntr; ++t) {
+    const TransformerW& tw = c->tw[t];
+    const int axis = t & 1;
+    // q, k, v with rotary, scattered per axis
+    GemmLaunch gq{};
+    gq.dtype = dt;
+    gq.epi = EPI_QKV;
+    gq.A = c->XH;
+    gq.B = wptr(tw.wqkv);
+    gq.M = NT;
+    gq.dense.N = 3 * c->I;
+    gq.dense.K = c->D;
+    gq.dense.lda = c->D;
+    gq.dense.ldb = c->D;
+    QkvArgs& qa = gq.qkv;
+    qa.q = axis ? c->qb : c->qt;
+    qa.k = axis ? c->kb : c->kt;
+    qa.vt = axis ? c->vtb : c->vtt;
+    qa.cos = axis ? c->cos_b : c->cos_t;
+    qa.sin = axis ? c->sin_b : c->sin_t;
+    qa.axis = axis;
+    qa.frames = c->T;
+    qa.batch = batch;
+    qa.heads = c->H;
+    qa.dh = c->DH;
+    qa.npad = axis ? 64 : c->Tp;
+    LAUNCH(MBR_K_QKV, launch_gemm(gq, s));
+
+    AttnLaunch al{};
+    al.dtype = dt;
+    al.axis = axis;
+    al.q = qa.q;
+    al.k = qa.k;
+    al.vt = qa.vt;
+    al.gates = c->gates;
+    al.o = c->O;
+    al.n = axis ? c->NB : c->T;
+    al.npad = qa.npad;
+    al.seqs = axis ? BT : c->NB * batch;
+    al.heads = c->H;
+    al.dh = c->DH;
+    al.frames = c->T;
+    al.batch = batch;
+    al.scale_log2 = 1.4426950408889634f;  // the 1/sqrt(dh) scale is folded into W_q
+    LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME, launch_attention(al, s));
+
+    GemmLaunch go{};
+    go.dtype = dt;
+    go.epi = EPI_RESID;
+    go.A = c->O;
+    go.B = wptr(tw.wout);
+    go.C = c->X;
+    go.bias = nullptr;
+    go.ldc = c->D;
+    go.M = NT;
+    go.dense.N = c->D;
+    go.dense.K = c->I;
+    go.dense.lda = c->I;
+    go.dense.ldb = c->I;
+    LAUNCH(MBR_K_OUT_PROJ, launch_gemm(go, s));
+
+    NormLaunch n0{dt, 0, c->X, c->XH, nullptr, nullptr, nullptr, nullptr, NT, c->D, c->H};
+    LAUNCH(MBR_K_NORM, launch_norm(n0, s));
+
+    GemmLaunch g1{};
+    g1.dtype = dt;
+    g1.epi = EPI_GELU;
+    g1.A = c->XH;
+    g1.B = wptr(tw.w1);
+    g1.C = c->H1;
+    g1.bias = c->fdev;
+    g1.dense.bias_off = (int64_t)tw.b1;
+    g1.ldc = c->FF;
+    g1.M = NT;
+    g1.dense.N = c->FF;
+    g1.dense.K = c->D;
+    g1.dense.lda = c->D;
+    g1.dense.ldb = c->D;
+    LAUNCH(MBR_K_FFN1, launch_gemm(g1, s));
+
+    GemmLaunch g2{};
+    g2.dtype = dt;
+    g2.epi = EPI_RESID;
+    g2.A = c->H1;
+    g2.B = wptr(tw.w2);
+    g2.C = c->X;
+    g2.bias = c->fdev;
+    g2.dense.bias_off = (int64_t)tw.b2;
+    g2.ldc = c->D;
+    g2.M = NT;
+    g2.dense.N = c->D;
+    g2.dense.K = c->FF;
+    g2.dense.lda = c->FF;
+    g2.dense.ldb = c->FF;
+    LAUNCH(MBR_K_FFN2, launch_gemm(g2, s));
+
+    const bool last = t == ntr - 1;
+    NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
+                  last ? nullptr : c->fdev + c->tw[t + 1].wg, last ? nullptr : c->fdev + c->tw[t + 1].bg,
+                  NT, c->D, c->H};
+    LAUNCH(MBR_K_NORM, launch_norm(no, s));
+    if (stop_stage == 1 + t) return MBR_OK;
+  }
+
+  const int nlay = cfg.mask_depth + 1;
+  for (int st = 0; st < cfg.num_stems; ++st) {
+    const void* src = c->XH;
+    for (int j = 0; j < nlay; ++j) {
+      GemmLaunch gm{};
+      gm.dtype = dt;
+      gm.A = src;
+      gm.B = W;
+      gm.bias = c->fdev;
+      gm.M = BT;
+      gm.groups = c->groups;
+      gm.tiles = c->tiles + c->t_mask[st][j];
+      gm.n_tiles = c->n_mask[st][j];
+      if (j < nlay - 1) {
+        void* dst = (j % 2 == 0) ? c->H1 : c->H2;
+        gm.epi = EPI_TANH;
+        gm.C = dst;
+        gm.ldc = c->MH;
+        src = dst;
+      } else {
+        gm.epi = EPI_GLU;
+        gm.C = c->Mglu;
+        gm.glu_total = c->total;
+        gm.glu_frames = c->T;
+      }
+      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, launch_gemm(gm, s));
+    }
+  }
+  if (stop_stage == 1000) return MBR_OK;
+
+  AverageLaunch av{c->Mglu, out, c->inv_slot, c->inv_weight, batch, cfg.num_stems, c->total, c->T,
+                   c->bands.n_freqs, c->bands.channels, cfg.io_layout};
+  LAUNCH(MBR_K_AVERAGE, launch_average(av, s));
+  return MBR_OK;
+}
+
+}  // namespace
+
+// ====================================================================================== C ABI
+extern "C" {
+
+const char* mbr_last_error(void) { return g_err.c_str(); }
+
+int mbr_core_weight_count(const mbr_config* cfg) {
+  if (!cfg) return fail(MBR_E_ARG, "cfg is NULL");
+  Bands b;
+  std::string err;
+  int rc = build_bands(*cfg, &b, &err);
+  if (rc) return fail(rc, err);
+  return (int)inventory(*cfg, b).size();
+}
+
+int mbr_core_weight_info(const mbr_config* cfg, int index, int* ndim, int64_t dims[2], int* kind) {
+  if (!cfg || !ndim || !dims || !kind) return fail(MBR_E_ARG, "NULL argument");
+  Bands b;
+  std::string err;
+  int rc = build_bands(*cfg, &b, &err);
+  if (rc) return fail(rc, err);
+  auto inv = inventory(*cfg, b);
+  if (index < 0 || index >= (int)inv.size()) return fail(MBR_E_ARG, "weight index out of range");
+  *ndim = inv[index].ndim;
+  dims[0] = inv[index].rows;
+  dims[1] = inv[index].cols;
+  *kind = inv[index].kind;
+  return MBR_OK;
+}
+
+int mbr_core_table_sizes(const mbr_config* cfg, int32_t* num_bands, int32_t* total_width, int32_t* n_freqs) {
+  if (!cfg) return fail(MBR_E_ARG, "cfg is NULL");
+  Bands b;
+  std::string err;
+  int rc = build_bands(*cfg, &b, &err);
+  if (rc) return fail(rc, err);
+  if (num_bands) *num_bands = b.num_bands();
+  if (total_width) *total_width = b.total_width();
+  if (n_freqs) *n_freqs = b.n_freqs;
+  return MBR_OK;
+}
+
+int mbr_core_tables(const mbr_config* cfg, int32_t* band_bins, int32_t* band_offset, int32_t* gather_pair,
+                    int32_t* inv_slot, float* inv_weight, int32_t* bin_count) {
+  if (!cfg) return fail(MBR_E_ARG, "cfg is NULL");
+  Bands b;
+  std::string err;
+  int rc = build_bands(*cfg, &b, &err);
+  if (rc) return fail(rc, err);
+  for (int i = 0; i < b.num_bands(); ++i) {
+    if (band_bins) band_bins[i] = (int32_t)b.bins[i].size();
+  }
+  if (band_offset)
+    for (int i = 0; i <= b.num_bands(); ++i) band_offset[i] = b.offset[i];
+  if (gather_pair) std::memcpy(gather_pair, b.gather_pair.data(), b.gather_pair.size() * 4);
+  if (inv_slot) std::memcpy(inv_slot, b.inv_slot.data(), b.inv_slot.size() * 4);
+  if (inv_weight) std::memcpy(inv_weight, b.inv_weight.data(), b.inv_weight.size() * 4);
+  if (bin_count) std::memcpy(bin_count, b.count.data(), b.count.size() * 4);
+  return MBR_OK;
+}
+
+int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_weights, mbr_core** out) {
+  if (!out) return fail(MBR_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !weights) return fail(MBR_E_ARG, "NULL argument");
+  mbr_core* c = new (std::nothrow) mbr_core();
+  if (!c) return fail(MBR_E_NOMEM, "host allocation failed");
+  c->cfg = *cfg;
+  std::string err;
+  int rc = build_bands(*cfg, &c->bands, &err);
+  if (rc) {
+    delete c;
+    return fail(rc, err);
+  }
+  if (cfg->num_bands > 64) {
+    delete c;
+    return fail(MBR_E_CONFIG, "invalid config: the band-axis attention supports at most 64 bands");
+  }
+  rc = check_device(&c->device);
+  if (rc) {
+    delete c;
+    return rc;
+  }
+  auto inv = inventory(*cfg, c->bands);
+  if (n_weights != (int)inv.size()) {
+    delete c;
+    return fail(MBR_E_ARG, "expected " + std::to_string(inv.size()) + " weight tensors, got " + std::to_string(n_weights));
+  }
+  c->NB = cfg->num_bands;
+  c->D = cfg->dim;
+  c->H = cfg->heads;
+  c->DH = cfg->dim_head;
+  c->I = c->H * c->DH;
+  c->FF = cfg->ff_mult * c->D;
+  c->MH = cfg->mask_hidden_mult * c->D;
+  c->T = cfg->frames;
+  c->Tp = round_up(c->T, 128);
+  c->Bmax = cfg->max_batch;
+  c->total = c->bands.total_width();
+  const int kstep = cfg->dtype == MBR_F32 ? 16 : 32;
+  c->kpad.resize(c->NB);
+  c->kcol.resize(c->NB);
+  c->wp.resize(c->NB);
+  int col = 0;
+  for (int i = 0; i < c->NB; ++i) {
+    c->kpad[i] = round_up(c->bands.width[i], kstep);
+    c->kcol[i] = col;
+    col += c->kpad[i];
+    c->kpad_max = std::max(c->kpad_max, c->kpad[i]);
+    c->wp[i] = round_up(c->bands.width[i], 16);
+  }
+  c->kpad_total = col;
+  // read the caller's weights
+  std::vector<std::vector<double>> W(inv.size());
+  const size_t esz = dtype_size(cfg->dtype);
+  for (size_t i = 0; i < inv.size(); ++i) {
+    if (!weights[i]) {
+      delete c;
+      return fail(MBR_E_ARG, "weight " + std::to_string(i) + " (" + inv[i].name + ") is NULL");
+    }
+    const size_t n = (size_t)inv[i].rows * inv[i].cols;
+    std::vector<char> raw(n * esz);
+    hipError_t e = hipMemcpy(raw.data(), weights[i], n * esz, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(MBR_E_HIP, "copying weight " + inv[i].name + ": " + hipGetErrorString(e));
+    }
+    W[i] = to_double(raw, cfg->dtype, n);
+  }
+  rc = repack_weights(c, W);
+  if (!rc) rc = setup_tables_and_groups(c);
+  if (!rc) rc = alloc_workspace(c);
+  if (!rc) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = fail(MBR_E_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
+  }
+  if (rc) {
+    mbr_core_destroy(c);
+    return rc;
+  }
+  *out = c;
+  return MBR_OK;
+}
+
+int mbr_core_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t stream) {
+  if (!c || !in || !out) return fail(MBR_E_ARG, "NULL argument");
+  if (batch < 1 || batch > c->Bmax) return fail(MBR_E_ARG, "batch out of range 1..max_batch");
+  return run_forward(c, in, out, batch, stream, -1);
+}
+
+int64_t mbr_core_debug_size(const mbr_core* c, int batch, int stage) {
+  if (!c || batch < 1 || batch > c->Bmax) return fail(MBR_E_ARG, "bad core or batch");
+  const int64_t BT = (int64_t)batch * c->T;
+  if (stage >= 0 && stage <= 2 * c->cfg.depth) return (int64_t)c->NB * BT * c->D;
+  if (stage == 1000) return BT * c->total;
+  return fail(MBR_E_ARG, "unknown stage");
+}
+
+int mbr_core_forward_debug(mbr_core* c, const float* in, int batch, int stage, float* out, hipStream_t stream) {
+  if (!c || !in || !out) return fail(MBR_E_ARG, "NULL argument");
+  int64_t n = mbr_core_debug_size(c, batch, stage);
+  if (n < 0) return (int)n;
+  int rc = run_forward(c, in, nullptr, batch, stream, stage);
+  if (rc) return rc;
+  const void* src = stage == 1000 ? (const void*)c->Mglu : (const void*)c->X;
+  HIP_TRY(hipMemcpyAsync(out, src, (size_t)n * 4, hipMemcpyDeviceToDevice, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  return MBR_OK;
+}
+
+int mbr_core_forward_profiled(mbr_core* c, const float* in, float* out, int batch, hipStream_t stream,
+                              double* ms_per_kind, int32_t* launches_per_kind) {
+  if (!c || !in || !out || !ms_per_kind || !launches_per_kind) return fail(MBR_E_ARG, "NULL argument");
+  if (batch < 1 || batch > c->Bmax) return fail(MBR_E_ARG, "batch out of range 1..max_batch");
+  Prof p;
+  p.s = stream;
+  int rc = run_forward(c, in, out, batch, stream, -1, &p);
+  hipError_t e = hipStreamSynchronize(stream);
+  for (int k = 0; k < MBR_K_COUNT; ++k) {
+    ms_per_kind[k] = 0.0;
+    launches_per_kind[k] = 0;
+  }
+  for (auto& m : p.marks) {
+    float ms = 0.f;
+    if (!rc && e == hipSuccess && hipEventElapsedTime(&ms, m.second.first, m.second.second) == hipSuccess) {
+      ms_per_kind[m.first] += ms;
+      launches_per_kind[m.first] += 1;
+    }
+    (void)hipEventDestroy(m.second.first);
+    (void)hipEventDestroy(m.second.second);
+  }
+  if (rc) return rc;
+  if (e != hipSuccess) return fail(MBR_E_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+  return MBR_OK;
+}
+
+int64_t mbr_core_device_bytes(const mbr_core* c) {
+  if (!c) return 0;
+  return (int64_t)(c->w_bytes + c->f_bytes + c->ws_bytes);
+}
+
+void mbr_core_destroy(mbr_core* c) {
+  if (!c) return;
+  if (c->wdev) (void)hipFree(c->wdev);
+  if (c->fdev) (void)hipFree(c->fdev);
+  if (c->ws) (void)hipFree(c->ws);
+  if (c->tables_dev) (void)hipFree(c->tables_dev);
+  delete c;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+"""Algorithmic work of the core's kernels, for throughput and roofline reporting.
+
+FLOPs follow the convention of [P1] section "FLOP shares": multiply-accumulates of every linear
+layer and of the two attention products (q k^T and p v), FLOPs = 2 x MACs, nothing for softmax,
+norms or activations.  Bytes of the memory-bound passes are the minimal traffic: each input read
+once and each output written once.
+
+MI355X peaks (AMD's published dense figures): HBM 8 TB/s; MFMA fp16 / bf16 2.5 PFLOP/s, fp32
+157.3 TFLOP/s.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict
+
+from . import synth
+
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {synth.F32: 157.3, synth.F16: 2500.0, synth.BF16: 2500.0}
+
+
+@dataclass
+class Shape:
+    B: int
+    T: int
+    NB: int
+    D: int
+    H: int
+    dh: int
+    FF: int
+    MH: int
+    total_width: int      # sum of band input widths
+    depth: int
+    mask_depth: int
+    stems: int
+    n_freqs: int
+    channels: int
+    esz: int              # bytes per operand element
+
+    @property
+    def tokens(self) -> int:
+        return self.NB * self.B * self.T
+
+    @property
+    def inner(self) -> int:
+        return self.H * self.dh
+
+
+def shape_of(w: synth.Workload, total_width: int, batch: int | None = None) -> Shape:
+    return Shape(B=w.batch if batch is None else batch, T=w.frames, NB=w.num_bands, D=w.dim, H=w.heads,
+                 dh=w.dim_head, FF=w.ff_mult * w.dim, MH=w.mask_hidden_mult * w.dim, total_width=total_width,
+                 depth=w.depth, mask_depth=w.mask_depth, stems=w.num_stems, n_freqs=w.freqs,
+                 channels=w.audio_channels, esz=4 if w.dtype == synth.F32 else 2)
+
+
+def flops_per_launch(s: Shape) -> Dict[str, float]:
+    """FLOPs of one launch of each kernel class (per Transformer for the trunk kernels)."""
+    N, D, I, H = s.tokens, s.D, s.inner, s.H
+    BT = s.B * s.T
+    return {
+        "embed": 2.0 * BT * D * s.total_width,
+        "norm_gates": 2.0 * N * D * H,                       # gate projection inside the norm pass
+        "qkv": 2.0 * N * D * 3 * I,
+        "attn_time": 2.0 * 2.0 * (s.NB * s.B) * H * s.T * s.T * s.dh,
+        "attn_band": 2.0 * 2.0 * BT * H * s.NB * s.NB * s.dh,
+        "out_proj": 2.0 * N * I * D,
+        "ffn1": 2.0 * N * D * s.FF,
+        "ffn2": 2.0 * N * s.FF * D,
+        "mask_hidden_first": 2.0 * BT * s.NB * D * s.MH,
+        "mask_hidden_next": 2.0 * BT * s.NB * s.MH * s.MH,
+        "mask_glu": 2.0 * BT * s.MH * 2 * s.total_width,
+    }
+
+
+def flops_forward(s: Shape) -> Dict[str, float]:
+    """FLOPs of a whole forward by part (trunk counts both axes of every layer)."""
+    f = flops_per_launch(s)
+    L = s.depth
+    per_axis = f["qkv"] + f["norm_gates"] + f["out_proj"] + f["ffn1"] + f["ffn2"]
+    trunk = 2 * L * per_axis + L * (f["attn_time"] + f["attn_band"])
+    mask = s.stems * (f["mask_hidden_first"] + (s.mask_depth - 1) * f["mask_hidden_next"] + f["mask_glu"])
+    return {"embed": f["embed"], "trunk": trunk, "mask": mask, "total": f["embed"] + trunk + mask,
+            "attn": L * (f["attn_time"] + f["attn_band"])}
+
+
+def bytes_per_launch(s: Shape) -> Dict[str, float]:
+    """Minimal HBM bytes of one launch of each memory-bound pass."""
+    N, D = s.tokens, s.D
+    BT = s.B * s.T
+    spec = 4.0 * BT * s.n_freqs * s.channels * 2
+    return {
+        "gather": spec + BT * s.total_width * s.esz,
+        "norm_pre": N * D * 4.0 + N * D * s.esz,                 # read x, write x^
+        "norm_out": N * D * 4.0 * 2 + N * D * s.esz,             # read x, write x and x^
+        "average": 4.0 * s.stems * BT * s.total_width + s.stems * spec,
+        "attn_band": 4.0 * N * s.inner * s.esz,                   # q, k, v read, o written
+    }

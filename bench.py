@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of the Mel-Band RoFormer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_11s_fp16]
+
+A step is one forward of the whole core (band gather and embedding, every axial Transformer, the
+mask head, the mask average) over one batch of seeded synthetic spectra already resident in HBM.
+Prints one JSON line: core audio-seconds per second, the per-kernel device times measured with HIP
+events on the launch stream, the roofline of the dominant kernel and the fp64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from axial_band_split_amd import binding, roofline, synth  # noqa: E402
+
+METRIC = "core audio-seconds/sec (44.1 kHz stereo) at T=1100; attn+GEMM TFLOP/s vs peak"
+MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu")
+GEMM_ATTN_KINDS = MFMA_KINDS + ("attn_band",)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kind_flops(s: roofline.Shape, kind: str, w: synth.Workload) -> float:
+    f = roofline.flops_per_launch(s)
+    if kind == "mask_hidden":   # average over the hidden layers of a stem
+        return (f["mask_hidden_first"] + (w.mask_depth - 1) * f["mask_hidden_next"]) / w.mask_depth
+    return f[kind]
+
+
+def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
+    """The oracle on a bounded sample: the band embedding, the first layer's time and band
+    Transformers, the mask head and the average of one forward, each timed once; the forward's
+    time is embedding + depth x (time + band Transformer) + mask head + average (every layer has
+    the same shape and cost)."""
+    from oracle import model as M
+
+    cfg = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads,
+                       w.dim_head, w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+    tables = cfg.tables()
+    wn = M.named(cfg, ws)
+    spec = M.read_input(x_io, w.audio_channels, w.io_layout)
+    t0 = time.perf_counter()
+    x = M.band_embed(spec, cfg, wn, tables)
+    t1 = time.perf_counter()
+    x = M.time_transformer(x, cfg, wn, "layer0.time.", chunk=1)
+    t2 = time.perf_counter()
+    x = M.band_transformer(x, cfg, wn, "layer0.band.", chunk=64)
+    t3 = time.perf_counter()
+    m = M.mask_head(x, cfg, wn, tables, 0)
+    M.average(m, tables)
+    t4 = time.perf_counter()
+    est = (t1 - t0) + w.depth * ((t2 - t1) + (t3 - t2)) + w.num_stems * (t4 - t3)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        pass
+    cores = max(threads or 1, M._WORKERS)
+    return {"value": w.audio_seconds / est, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {w.name}: band embedding, layer 0 time + band Transformers, "
+                       f"mask head and average timed once ({t4 - t0:.1f} s), forward estimated as "
+                       f"embed + {w.depth} x layer + mask head = {est:.1f} s"),
+            "host_cpus": os.cpu_count(), "blas_threads": threads, "seconds_sampled": t4 - t0}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3_11s_fp16", choices=list(synth.WORKLOADS))
+    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; the core runs on one GPU (no sharding, no "
+              f"collectives). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: B={w.batch} T={w.frames} D={w.dim} depth={w.depth} "
+        f"dtype={synth.DTYPE_NAMES[w.dtype]}")
+    cfg = binding.config(w)
+    inv = binding.inventory(cfg)
+    _, total_width, _ = binding.mbr_core_table_sizes(cfg)
+    ws = synth.draw_weights(inv, w.dtype, seed=w.weight_seed)
+    x_np = synth.input_in_layout(w, synth.draw_input(w))
+    core = binding.Core(cfg, ws)
+    log(f"[bench] core created: {core.device_bytes() / 2**30:.2f} GiB on the device")
+    x = torch.from_numpy(x_np).cuda()
+    out = torch.empty(core.output_shape(w.batch), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        core.forward(x, out, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        core.forward(x, out, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = w.audio_seconds * args.steps / (t1 - t0)
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, {value:.1f} audio-s/s")
+
+    # per-kernel device time: HIP event pairs around every launch on the launch stream
+    acc = {k: [0.0, 0] for k in binding.KERNEL_KINDS}
+    tp0 = time.perf_counter()
+    for _ in range(args.profile_steps):
+        prof = core.profile(x, out, stream)
+        for k, (ms, n) in prof.items():
+            acc[k][0] += ms
+            acc[k][1] += n
+    tp1 = time.perf_counter()
+    P = args.profile_steps
+    s = roofline.shape_of(w, total_width)
+    fl = roofline.flops_forward(s)
+    kernels = {}
+    for k, (ms, n) in acc.items():
+        if n == 0:
+            continue
+        e = {"ms_per_step": ms / P, "launches_per_step": n // P, "avg_launch_ms": ms / n}
+        if k in MFMA_KINDS or k == "attn_band":
+            e["tflops"] = kind_flops(s, k, w) / (ms / n * 1e-3) / 1e12
+        kernels[k] = e
+    dev_ms = sum(v["ms_per_step"] for v in kernels.values())
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dominant]
+    peak_mfma = roofline.PEAK_MFMA_TFLOPS[w.dtype]
+    if dominant in MFMA_KINDS:
+        ach = kind_flops(s, dominant, w) / (dk["avg_launch_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": ach, "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": ach / peak_mfma, "traffic": None,
+                "flops_per_launch": kind_flops(s, dominant, w), "avg_launch_ms": dk["avg_launch_ms"]}
+    else:
+        b = roofline.bytes_per_launch(s)
+        key = {"norm": "norm_pre", "gather": "gather", "average": "average", "attn_band": "attn_band"}[dominant]
+        ach = b[key] / (dk["avg_launch_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": roofline.PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / roofline.PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": b[key],
+                "avg_launch_ms": dk["avg_launch_ms"]}
+    ga_ms = sum(kernels[k]["ms_per_step"] for k in GEMM_ATTN_KINDS if k in kernels)
+    ga_tflops = fl["total"] / (ga_ms * 1e-3) / 1e12
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+        log(f"[bench]   {k:12s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:4d} launches"
+            + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, bounded sample) ...")
+        cpu = cpu_baseline(w, ws, x_np)
+        log(f"[bench] cpu baseline: {cpu['value']:.4f} audio-s/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "audio-s/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": synth.DTYPE_NAMES[w.dtype], "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "frames": w.frames, "bands": w.num_bands, "dim": w.dim,
+                   "depth": w.depth, "heads": w.heads, "dim_head": w.dim_head, "io_layout": w.io_layout,
+                   "audio_seconds_per_step": w.audio_seconds},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "attn_gemm": {"tflops": ga_tflops, "peak": peak_mfma, "frac": ga_tflops / peak_mfma,
+                      "flops_per_step": fl["total"], "device_ms": ga_ms},
+        "e2e_tflops": fl["total"] / (ms_step * 1e-3) / 1e12,
+        "device_ms_per_step": dev_ms,
+        "profiled_ms_per_step": (tp1 - tp0) * 1e3 / P,
+        "kernels": kernels,
+    }
+    core.close()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,208 @@
+/*
+ * mbr_core.h — C ABI of the Mel-Band RoFormer mask-estimation core on AMD MI355X (gfx950).
+ *
+ * The core is the network between an STFT and its inverse in a music source separator:
+ * complex stereo STFT bins in, per-bin complex masks out.  What it computes is stated on
+ *   [P1] "Mel-Band RoFormer — architecture, inference hot path & RTX 3050 feasibility",
+ *        sections "The forward chain", "The mel-band split, exactly", "The two transformers
+ *        are not the same shape", "Parameter accounting";
+ *   [P3] "Vocal Separation Core (Mel-Band RoFormer) — ONNX / fp16 / WebGPU", section
+ *        "How to use" and its signature table (stft_repr -> masks, both [B, F*S, T, 2]);
+ *   [P4] "Mel-Band RoFormer (vocals), ONNX for the GPU (float16 weights)", section "Graph"
+ *        (the plane layout [B, S*2, F, T]);
+ *   [P5] "@audio/neural-separate 0.4.0 -> 0.5.0", scripts/export-roformer.py (class Core)
+ *        and roformer.js (the session shape {run, free}, null without a capable GPU).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative MBR_E_* code; mbr_last_error() then describes the
+ *     failure (per calling thread).  No C++ exception crosses this boundary.
+ *   - Pointers named "host" are host memory, pointers named "dev" are device memory on the
+ *     GPU that is current when the call is made.  The caller owns every pointer it passes.
+ *   - A handle is bound to the device that was current at mbr_core_create; use it with
+ *     that device current.  Calls on one handle must not overlap (the workspace is shared).
+ */
+#ifndef MBR_CORE_H
+#define MBR_CORE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------------------ */
+#define MBR_OK         0
+#define MBR_E_ARG     (-1) /* null pointer, bad index, batch out of range                  */
+#define MBR_E_CONFIG  (-2) /* invalid configuration: a band without bins, a bin in more than
+                              two bands or in none, sizes out of range, unknown dtype/layout */
+#define MBR_E_DEVICE  (-3) /* the current device is not a gfx950 (MI355X-class) GPU          */
+#define MBR_E_HIP     (-4) /* a HIP runtime call failed                                      */
+#define MBR_E_NOMEM   (-5) /* device or host allocation failed                              */
+
+/* ---- enumerations ----------------------------------------------------------------- */
+enum { MBR_F32 = 0, MBR_F16 = 1, MBR_BF16 = 2 };          /* weight / GEMM operand dtype    */
+enum { MBR_IO_FS_T_C = 0, MBR_IO_SC_F_T = 1 };            /* boundary tensor layout         */
+enum { MBR_KIND_MATRIX = 0, MBR_KIND_BIAS = 1, MBR_KIND_GAMMA = 2 };
+
+/*
+ * Configuration of one core.
+ *   sample_rate, n_fft      STFT the bands are built for (F = n_fft/2 + 1 bins).
+ *   audio_channels (S)      stereo = 2; merged into the frequency axis as pair = f*S + s.
+ *   num_bands (NB)          Slaney-mel bands ([P1] "The mel-band split, exactly").
+ *   dim (D), depth (L)      residual width and number of axial blocks (time + band each).
+ *   heads (H), dim_head     attention heads; inner width H*dim_head ([P1] "Per Attention layer").
+ *   ff_mult                 feed-forward hidden = ff_mult * D.
+ *   mask_hidden_mult        mask-MLP hidden = mask_hidden_mult * D.
+ *   mask_depth              number of Linear+Tanh layers before the last Linear of the mask MLP
+ *                           (2 in every published configuration: three Linear layers).
+ *   num_stems               mask heads sharing one trunk (1 = one set of masks).
+ *   max_batch, frames (T)   largest batch a forward may use, frames per chunk.
+ *   dtype                   MBR_F32: fp32 everywhere; MBR_F16 / MBR_BF16: weights and GEMM /
+ *                           attention operands in that type, fp32 accumulation, softmax, norms
+ *                           and residual stream.
+ *   io_layout               MBR_IO_FS_T_C: [B, F*S, T, 2] (last axis re, im) ([P3]);
+ *                           MBR_IO_SC_F_T: [B, S*2, F, T] (planes L re, L im, R re, R im) ([P4]).
+ */
+typedef struct mbr_config {
+  int32_t sample_rate;
+  int32_t n_fft;
+  int32_t audio_channels;
+  int32_t num_bands;
+  int32_t dim;
+  int32_t depth;
+  int32_t heads;
+  int32_t dim_head;
+  int32_t ff_mult;
+  int32_t mask_hidden_mult;
+  int32_t mask_depth;
+  int32_t num_stems;
+  int32_t max_batch;
+  int32_t frames;
+  int32_t dtype;
+  int32_t io_layout;
+} mbr_config;
+
+typedef struct mbr_core mbr_core;
+
+/* Text of the last error on the calling thread ("" if none).  The string stays valid until
+ * the next failing call on that thread. */
+const char* mbr_last_error(void);
+
+/* ---- weight inventory ------------------------------------------------------------- */
+/*
+ * The weights are a fixed list of tensors in canonical order, following the module tree of
+ * [P1] "Parameter accounting" / "Per Attention layer" and [P5] class Core (Linear weights are
+ * [out, in], row-major):
+ *   for each band i (W_i = 2*S*bins_i):   norm.gamma [W_i], proj.weight [D, W_i], proj.bias [D]
+ *   for each layer l, for axis in (time, band):
+ *       attn.norm.gamma [D], attn.to_qkv.weight [3*H*dh, D], attn.to_gates.weight [H, D],
+ *       attn.to_gates.bias [H], attn.to_out.weight [D, H*dh], ff.norm.gamma [D],
+ *       ff.fc1.weight [FF, D], ff.fc1.bias [FF], ff.fc2.weight [D, FF], ff.fc2.bias [D],
+ *       norm.gamma [D]
+ *   for each stem, for each band i, for j in 0..mask_depth:
+ *       mlp{j}.weight [out_j, in_j], mlp{j}.bias [out_j]
+ *       with (in, out) = (D, MH), (MH, MH) ..., (MH, 2*W_i); the last layer's first W_i
+ *       outputs are the GLU values and the second W_i its gates.
+ * mbr_core_weight_count returns the number of tensors (or a negative error code).
+ * mbr_core_weight_info writes tensor `index`'s shape: rank (1 or 2) to *ndim, sizes to dims[0..1]
+ * (dims[1] = 1 for vectors) and its kind (MBR_KIND_*) to *kind.
+ */
+int mbr_core_weight_count(const mbr_config* cfg);
+int mbr_core_weight_info(const mbr_config* cfg, int index, int* ndim, int64_t dims[2], int* kind);
+
+/* ---- band tables ------------------------------------------------------------------ */
+/*
+ * Sizes of the tables of mbr_core_tables: *num_bands, *total_width (sum of W_i, features of
+ * all bands), *n_freqs (F).
+ */
+int mbr_core_table_sizes(const mbr_config* cfg, int32_t* num_bands, int32_t* total_width, int32_t* n_freqs);
+/*
+ * The band tables of [P1] "The mel-band split, exactly": a binarised Slaney-mel filter bank with
+ * DC forced into band 0 and Nyquist into the last band; each band's bins ascending, channels
+ * interleaved (pair = bin*S + s); features = pair rank*2 + (re, im).  All buffers are host
+ * memory the caller allocates (any may be NULL to skip it):
+ *   band_bins     [NB]        bins in each band
+ *   band_offset   [NB + 1]    first feature of each band in the concatenation of all bands
+ *   gather_pair   [ΣW / 2]    pair index (bin*S + s) of every (band, pair rank) slot, bands in order
+ *   inv_slot      [F*S*2]     for each pair p: the slots (into gather_pair) holding p, at most two;
+ *                             entries 2p and 2p+1, -1 where a bin has only one band
+ *   inv_weight    [F*S]       1 / (number of bands covering the pair's bin)
+ *   bin_count     [F]         number of bands covering each bin (1 or 2)
+ */
+int mbr_core_tables(const mbr_config* cfg, int32_t* band_bins, int32_t* band_offset, int32_t* gather_pair,
+                    int32_t* inv_slot, float* inv_weight, int32_t* bin_count);
+
+/* ---- lifetime --------------------------------------------------------------------- */
+/*
+ * Build a core on the current device.  weights[i] is a DEVICE pointer to tensor i of the
+ * inventory, stored in cfg->dtype (float32, float16 or bfloat16 bit patterns), row-major.
+ * The library copies and repacks them (norm gains and the attention scale folded into the
+ * following projections, per-band tiles padded, mask gates paired with their values), so the
+ * caller may free them as soon as this returns.  Synchronous.  Allocates all device memory the
+ * forward needs for up to cfg->max_batch chunks of cfg->frames frames.
+ * Errors: MBR_E_ARG, MBR_E_CONFIG, MBR_E_DEVICE, MBR_E_HIP, MBR_E_NOMEM; *out is NULL then.
+ */
+int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_weights, mbr_core** out);
+
+/*
+ * One forward of the core ([P1] "The forward chain", from the mel gather to the division by
+ * the band count).  stft_repr (dev, float32) and masks (dev, float32) are in cfg->io_layout:
+ *   MBR_IO_FS_T_C: [batch, F*S, T, 2]       MBR_IO_SC_F_T: [batch, S*2, F, T]
+ * with a leading stem axis after batch in masks when num_stems > 1.  1 <= batch <= max_batch.
+ * Enqueued on `stream` (0 = the null stream); returns without waiting.  No allocation, no host
+ * synchronisation and no atomics: the same input gives bitwise the same masks.  The caller keeps
+ * both buffers alive until the stream has passed this work.  The masks are not multiplied with
+ * the spectrum.
+ */
+int mbr_core_forward(mbr_core* core, const float* stft_repr_dev, float* masks_dev, int batch, hipStream_t stream);
+
+/* Release the core's device memory.  NULL is accepted. */
+void mbr_core_destroy(mbr_core* core);
+
+/* ---- test taps -------------------------------------------------------------------- */
+/*
+ * Run the forward up to a stage and copy that stage's tensor (float32) to out_dev:
+ *   stage 0            band embedding x, layout [NB][batch][T][D]
+ *   stage 1 + k        x after Transformer k (k = 2*l for layer l's time axis, 2*l + 1 band axis)
+ *   stage 1000         the GLU output of stem 0, layout [batch][ΣW][T] (feature-major)
+ * mbr_core_debug_size gives the number of floats of a stage for a batch (negative on error).
+ * Synchronous on `stream`.
+ */
+int64_t mbr_core_debug_size(const mbr_core* core, int batch, int stage);
+int mbr_core_forward_debug(mbr_core* core, const float* stft_repr_dev, int batch, int stage, float* out_dev,
+                           hipStream_t stream);
+
+/* ---- per-kernel timing ------------------------------------------------------------ */
+/* Kernel classes of one forward, in launch order. */
+enum {
+  MBR_K_GATHER = 0,      /* band gather + per-band normalisation                        */
+  MBR_K_EMBED = 1,       /* per-band projection (grouped GEMM)                          */
+  MBR_K_NORM = 2,        /* RMSNorm passes over the residual stream (+ attention gates)  */
+  MBR_K_QKV = 3,         /* q/k/v projection with rotary                                 */
+  MBR_K_ATTN_TIME = 4,   /* attention along frames                                       */
+  MBR_K_ATTN_BAND = 5,   /* attention along bands                                        */
+  MBR_K_OUT_PROJ = 6,    /* attention output projection + residual                       */
+  MBR_K_FFN1 = 7,        /* feed-forward first layer + GELU                              */
+  MBR_K_FFN2 = 8,        /* feed-forward second layer + residual                         */
+  MBR_K_MASK_HIDDEN = 9, /* mask MLP hidden layers (grouped GEMM, tanh)                  */
+  MBR_K_MASK_GLU = 10,   /* mask MLP last layer + GLU (grouped GEMM)                     */
+  MBR_K_AVERAGE = 11,    /* inverse-index mask average                                   */
+  MBR_K_COUNT = 12
+};
+/*
+ * The same forward as mbr_core_forward, with a HIP event pair recorded on `stream` around every
+ * kernel launch; waits for the stream, then writes per class the summed device milliseconds
+ * (ms_per_kind[MBR_K_COUNT]) and the number of launches (launches_per_kind[MBR_K_COUNT]), host
+ * arrays.  Meant for measurement, not for the serving path (it creates events and synchronises).
+ */
+int mbr_core_forward_profiled(mbr_core* core, const float* stft_repr_dev, float* masks_dev, int batch,
+                              hipStream_t stream, double* ms_per_kind, int32_t* launches_per_kind);
+
+/* Device bytes held by the core (weights + workspace). */
+int64_t mbr_core_device_bytes(const mbr_core* core);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MBR_CORE_H */

@@ -34,6 +34,8 @@ rotary base 10000 with inverse frequencies base^(-2j/dh) over interleaved pairs
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Dict, List, Sequence, Tuple
 
@@ -45,6 +47,7 @@ from . import mel
 KIND_MATRIX, KIND_BIAS, KIND_GAMMA = 0, 1, 2
 NORM_EPS = 1e-12
 ROPE_BASE = 10000.0
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
 @dataclass(frozen=True)
@@ -176,10 +179,26 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
     return x / np.maximum(n, NORM_EPS) * math.sqrt(x.shape[-1]) * gamma
 
 
+def _gelu_block(x: np.ndarray) -> np.ndarray:
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU, x * Phi(x) with the error function ([P5] class FF uses F.gelu).
-    The error function is scipy's (a library primitive; pinned against math.erf)."""
-    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+    The error function is scipy's (a library primitive; pinned against math.erf).  Large arrays
+    are evaluated in row blocks on a thread pool; every element is computed the same way."""
+    if x.size < (1 << 20):
+        return _gelu_block(x)
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty_like(flat)
+    step = max(1, flat.shape[0] // (4 * _WORKERS))
+
+    def run(a):
+        out[a:a + step] = _gelu_block(flat[a:a + step])
+
+    with ThreadPoolExecutor(_WORKERS) as ex:
+        list(ex.map(run, range(0, flat.shape[0], step)))
+    return out.reshape(x.shape)
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,179 @@
+"""Parity of the HIP core against the fp64 oracle, through the C ABI, on the seeded workloads.
+
+Bars: relative L2 of the masks <= 1e-4 on the fp32 path and <= 2e-2 on the fp16 / bf16 paths
+(the core's stated tolerances); band and index tables are checked bit-exact on the CPU.
+"""
+import numpy as np
+import pytest
+
+from axial_band_split_amd import binding, synth
+from oracle import model as M
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOL = {synth.F32: 1e-4, synth.F16: 2e-2, synth.BF16: 2e-2}
+
+
+def ocfg(w: synth.Workload) -> M.CoreConfig:
+    return M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads,
+                        w.dim_head, w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm((np.asarray(a, np.float64) - b).ravel()) / np.linalg.norm(np.asarray(b).ravel()))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def build(w: synth.Workload, max_batch=None, std=0.02, gamma_std=0.02):
+    cfg = binding.config(w, max_batch=max_batch)
+    ws = synth.draw_weights(binding.inventory(cfg), w.dtype, seed=w.weight_seed, std=std, gamma_std=gamma_std)
+    return cfg, ws
+
+
+def gpu_forward(core: binding.Core, x_io: np.ndarray) -> np.ndarray:
+    xd = torch.from_numpy(np.ascontiguousarray(x_io)).cuda()
+    y = core.forward(xd)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["c0_tiny_fp32", "c1_small_fp16", "c2_8s_bf16", "c3_11s_fp16"])
+def test_masks_match_oracle_full_size(name):
+    w = synth.WORKLOADS[name]
+    say(f"[parity] {name}: B={w.batch} T={w.frames} dtype={synth.DTYPE_NAMES[w.dtype]} layout={w.io_layout}")
+    cfg, ws = build(w)
+    x = synth.input_in_layout(w, synth.draw_input(w))
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, ocfg(w), ws, layout=w.io_layout)
+    err = rel_l2(y, ref)
+    say(f"[parity] {name}: rel L2 = {err:.3e} (tolerance {TOL[w.dtype]:.0e})")
+    assert np.isfinite(y).all()
+    assert err <= TOL[w.dtype]
+
+
+def test_heavy_architecture_matches_oracle_at_short_length():
+    """The heavy configuration's architecture (dim 512, depth 12, bf16, 4 chunks) at 96 frames,
+    where the oracle is quick; the full 1100-frame run is checked by properties below."""
+    w = synth.WORKLOADS["c4_heavy_bf16"].replace(frames=96, batch=2)
+    say(f"[parity] c4 architecture at T={w.frames}, B={w.batch}")
+    cfg, ws = build(w, max_batch=4)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, ocfg(w), ws)
+    err = rel_l2(y, ref)
+    say(f"[parity] c4 short: rel L2 = {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_tiny_config_in_half_precision(dtype):
+    w = synth.WORKLOADS["c0_tiny_fp32"].replace(dtype=dtype)
+    say(f"[parity] c0 in {synth.DTYPE_NAMES[dtype]}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    err = rel_l2(y, M.forward(x, ocfg(w), ws))
+    say(f"[parity] c0 {synth.DTYPE_NAMES[dtype]}: rel L2 = {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_fp32_stage_taps_match_oracle():
+    """Band embedding, every Transformer's output and the GLU output of the fp32 path, each
+    within 1e-5 relative L2 of the oracle's intermediate (the pages' stage-by-stage nulls)."""
+    w = synth.WORKLOADS["c0_tiny_fp32"].replace(depth=2)
+    say("[taps] c0 fp32, depth 2")
+    cfg, ws = build(w, std=0.05, gamma_std=0.3)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    xd = torch.from_numpy(x).cuda()
+    taps = M.Taps()
+    ref = M.forward(x, ocfg(w), ws, taps=taps)
+    B, T, NB, D = taps.embed.shape
+
+    def to_lib_layout(a):            # oracle [B, T, NB, D] -> library [NB, B, T, D]
+        return a.transpose(2, 0, 1, 3)
+
+    got = core.debug(xd, 0).cpu().numpy().reshape(NB, B, T, D)
+    assert rel_l2(got, to_lib_layout(taps.embed)) < 1e-5
+    for k, a in enumerate(taps.after):
+        got = core.debug(xd, 1 + k).cpu().numpy().reshape(NB, B, T, D)
+        e = rel_l2(got, to_lib_layout(a))
+        say(f"[taps] transformer {k}: {e:.2e}")
+        assert e < 1e-5
+    glu = core.debug(xd, 1000).cpu().numpy().reshape(B, -1, T)
+    want = np.concatenate(taps.glu, axis=-1).transpose(0, 2, 1)
+    assert rel_l2(glu, want) < 1e-5
+    y = gpu_forward(core, x)
+    core.close()
+    assert rel_l2(y, ref) < 1e-5
+
+
+def test_batch_below_max_and_sc_f_t_layout():
+    w = synth.WORKLOADS["c0_tiny_fp32"].replace(batch=3, io_layout=synth.IO_SC_F_T)
+    say("[parity] c0 layout 1, max_batch 3, batches 3, 2, 1")
+    cfg, ws = build(w)
+    x = synth.input_in_layout(w, synth.draw_input(w))
+    core = binding.Core(cfg, ws)
+    for b in (3, 2, 1):
+        y = gpu_forward(core, x[:b])
+        err = rel_l2(y, M.forward(x[:b], ocfg(w), ws, layout=1))
+        say(f"[parity] batch {b}: {err:.2e}")
+        assert err <= 1e-4
+    core.close()
+
+
+def test_silent_frames_and_a_silent_band_stay_finite():
+    """A fifth of the frames zeroed and one band's bins zeroed: the 1e-12 clamp keeps every row
+    finite (the pages report NaN masks from an fp16 norm here) and parity still holds."""
+    for dtype in (synth.F32, synth.F16):
+        w = synth.WORKLOADS["c0_tiny_fp32"].replace(dtype=dtype)
+        say(f"[edge] silent frames / band, {synth.DTYPE_NAMES[dtype]}")
+        cfg, ws = build(w)
+        x = synth.draw_input(w)
+        x[:, :, ::5, :] = 0.0
+        t = ocfg(w).tables()
+        x[:, t.pairs[3], :, :] = 0.0
+        core = binding.Core(cfg, ws)
+        y = gpu_forward(core, x)
+        core.close()
+        assert np.isfinite(y).all()
+        assert rel_l2(y, M.forward(x, ocfg(w), ws)) <= TOL[dtype]
+
+
+def test_forward_is_deterministic():
+    w = synth.WORKLOADS["c1_small_fp16"]
+    say("[det] c1 twice")
+    cfg, ws = build(w)
+    core = binding.Core(cfg, ws)
+    xd = torch.from_numpy(synth.draw_input(w)).cuda()
+    a = core.forward(xd).clone()
+    b = core.forward(xd)
+    torch.cuda.synchronize()
+    core.close()
+    assert torch.equal(a, b)
+
+
+def test_heavy_full_size_batch_consistency():
+    """The heavy configuration at full size (4 chunks of 1100 frames): finite, and each chunk's
+    masks are bitwise those of a batch-1 call on that chunk (chunks never interact)."""
+    w = synth.WORKLOADS["c4_heavy_bf16"]
+    say("[c4] full size, batch 4 vs batch 1")
+    cfg, ws = build(w)
+    core = binding.Core(cfg, ws)
+    xd = torch.from_numpy(synth.draw_input(w)).cuda()
+    y4 = core.forward(xd)
+    y1 = core.forward(xd[2:3].contiguous())
+    torch.cuda.synchronize()
+    assert torch.isfinite(y4).all()
+    assert torch.equal(y4[2:3], y1)
+    core.close()
