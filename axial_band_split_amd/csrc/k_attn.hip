@@ -2,7 +2,8 @@
 // gate, written back in token layout ([P1] "Per Attention layer": per-head sigmoid gates on the
 // attention output; [P5] export-roformer.py class Attn).
 //
-// Both kernels compute the transposed products S^T = K Q^T and O^T = V^T P^T on the matrix cores.
+// q, k and v arrive as [seq][head][position][dh].  Both kernels compute the transposed products
+// S^T = K Q^T and O^T = V^T P^T on the matrix cores; V is transposed while it is staged in LDS.
 // In the 16 x 16 accumulator layout a lane then owns one query column, so the softmax statistics
 // of a query (running max, running sum) and the rescaling of its output stay in that lane's
 // registers; only the max needs a reduction over the four lane groups of the wave.  The
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_time_kernel(AttnLaunch L) {
   const size_t base = ((size_t)seq * L.heads + h) * (size_t)npad * DH;
   const T* Q = (const T*)L.q + base;
   const T* K = (const T*)L.k + base;
-  const T* Vt = (const T*)L.vt + base;
+  const T* V = (const T*)L.v + base;
 
   frag qf[2][DSTEPS];
 #pragma unroll
@@ -102,11 +103,15 @@ __global__ __launch_bounds__(256) void attn_time_kernel(AttnLaunch L) {
       const int r = c / KCH, p = c - r * KCH;
       *(uint4*)(lds + r * KROW + p * 16) = *(const uint4*)((const char*)(K + (size_t)(kt * KT + r) * DH) + p * 16);
     }
-    constexpr int VCH = KT * (int)sizeof(T) / 16;
-    for (int c = threadIdx.x; c < DH * VCH; c += 256) {
-      const int r = c / VCH, p = c - r * VCH;
-      *(uint4*)(lds + KT * KROW + r * VROW + p * 16) =
-          *(const uint4*)((const char*)(Vt + (size_t)r * npad + kt * KT) + p * 16);
+    // V tile [64 keys][DH] -> LDS as V^T [DH][keys]
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int DCH = DH / EPC;
+    for (int c = threadIdx.x; c < KT * DCH; c += 256) {
+      const int r = c / DCH, p = c - r * DCH;
+      const uint4 raw = *(const uint4*)(V + (size_t)(kt * KT + r) * DH + p * EPC);
+      const T* vals = (const T*)&raw;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) *(T*)(lds + KT * KROW + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
     }
     __syncthreads();
 
@@ -203,7 +208,22 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
   const size_t base = (size_t)sh * 64 * DH;
   const T* Q = (const T*)L.q + base;
   const T* K = (const T*)L.k + base;
-  const T* Vt = (const T*)L.vt + base;
+  const T* V = (const T*)L.v + base;
+  constexpr int VROW = 64 * (int)sizeof(T) + 16;
+  __shared__ __attribute__((aligned(16))) char vlds_all[4][DH * VROW];
+  char* vlds = vlds_all[wave];
+  {
+    // this wave's V [64 keys][DH] -> V^T [DH][keys] in its own LDS slice
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int DCH = DH / EPC;
+    for (int c = lane; c < 64 * DCH; c += 64) {
+      const int r = c / DCH, p = c - r * DCH;
+      const uint4 raw = *(const uint4*)(V + (size_t)r * DH + p * EPC);
+      const T* vals = (const T*)&raw;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) *(T*)(vlds + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
+    }
+  }
 
   f32x4 s[4][4];
 #pragma unroll
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
     for (int c = 0; c < 4; ++c) pf[c] = PFrag<T>::make(s[m * SPP][c], s[m * SPP + SPP - 1][c]);
 #pragma unroll
     for (int d = 0; d < DH / 16; ++d) {
-      const auto a = PFrag<T>::vload((const char*)(Vt + (size_t)(d * 16 + l16) * 64), m, g4);
+      const auto a = PFrag<T>::vload(vlds + (d * 16 + l16) * VROW, m, g4);
 #pragma unroll
       for (int c = 0; c < 4; ++c) mma(oacc[d][c], a, pf[c]);
     }

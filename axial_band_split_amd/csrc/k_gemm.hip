@@ -8,7 +8,7 @@
 //
 // Epilogues (applied to the fp32 accumulators in registers):
 //   EMBED  band embedding: + bias, fp32 residual stream out
-//   QKV    rotary on q and k (interleaved pairs, partner column = neighbouring lane), q / k / v^T
+//   QKV    rotary on q and k (interleaved pairs, partner column = neighbouring lane), q / k / v
 //          scattered into the per-sequence attention layout of the current axis
 //   GELU   + bias, exact-erf GELU, operand dtype out
 //   RESID  + bias (optional), added into the fp32 residual stream
@@ -67,7 +67,7 @@ struct GemmKernel {
               T* dst = (T*)(which == 0 ? a.q : a.k);
               dst[(((size_t)seq * a.heads + h) * a.npad + pos) * a.dh + d] = cvt<T>(v);
             } else {
-              ((T*)a.vt)[(((size_t)seq * a.heads + h) * a.dh + d) * a.npad + pos] = cvt<T>(v);
+              ((T*)a.v)[(((size_t)seq * a.heads + h) * a.npad + pos) * a.dh + d] = cvt<T>(v);
             }
           }
         }

@@ -32,13 +32,13 @@ enum Epi {
   EPI_GELU = 2,      // C(T) = gelu(acc + bias)                       (FFN1)
   EPI_RESID = 3,     // C(float) += acc (+ bias)                      (out-proj, FFN2)
   EPI_TANH = 4,      // C(T) = tanh(acc + bias)                       (mask MLP hidden layers)
-  EPI_GLU = 5,       // paired value/gate columns -> value*sigmoid(gate), feature-major float
+  EPI_GLU = 5,       // paired value/gate column blocks -> value*sigmoid(gate), feature-major float
 };
 
 struct QkvArgs {
   void* q;            // [seqs][H][npad][dh]
   void* k;            // [seqs][H][npad][dh]
-  void* vt;           // [seqs][H][dh][npad]
+  void* v;            // [seqs][H][npad][dh]
   const float* cos;   // [npos][dh/2]
   const float* sin;
   int32_t axis;       // 0: time (seq = row / T, pos = row % T); 1: band (seq = row % (B*T), pos = row / (B*T))
@@ -65,7 +65,12 @@ struct GemmLaunch {
   int32_t glu_total, glu_frames;
 };
 
+// Generic 128 x 128 tile kernel (every dtype; the fp32 path uses it).  GLU pairs 16-column blocks.
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t stream);
+// 16-bit operand kernel (fp16 / bf16): 256 x 128 tiles; needs N % 64 == 0 and K % 32 == 0 for dense
+// launches; grouped tile tables must use 256-row tiles.  GLU pairs 32-column blocks.
+hipError_t launch_gemm2(const GemmLaunch& L, hipStream_t stream);
+int gemm2_tile_rows();
 
 // Row RMS norm passes over the fp32 residual stream x [rows, D].
 //   mode 0: xh = T(x * sqrt(D) / max(|x|, eps)); gates (optional) from the same normalised row
@@ -96,14 +101,14 @@ struct GatherLaunch {
 };
 hipError_t launch_gather(const GatherLaunch& L, hipStream_t stream);
 
-// Attention over sequences held in [seqs][H][npad][dh] (q, k) and [seqs][H][dh][npad] (v^T);
+// Attention over sequences held in [seqs][H][npad][dh] (q, k, v);
 // writes O * gate into token layout O[row][H*dh].
 struct AttnLaunch {
   int dtype;
   int axis;                 // 0 time (flash, n = T), 1 band (n = NB <= 64, one wave per sequence-head)
   const void* q;
   const void* k;
-  const void* vt;
+  const void* v;
   const float* gates;       // [rows][H]
   void* o;                  // [rows][H*dh]
   int32_t n, npad, seqs, heads, dh, frames, batch;

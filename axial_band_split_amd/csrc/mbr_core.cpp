@@ -116,6 +116,8 @@ struct mbr_core {
   int device = 0;
   int NB = 0, D = 0, H = 0, DH = 0, I = 0, FF = 0, MH = 0, T = 0, Tp = 0, Bmax = 0, total = 0;
   std::vector<int> kpad, kcol, wp;    // per band: padded K of the embedding, U column block, mask N/2
+  int tile_m = 128;                   // row tile of the grouped GEMM tables (kernel-dependent)
+  int glu_blk = 16;                   // value / gate pairing block of the last mask layer
   int kpad_total = 0, kpad_max = 0;
   // device memory
   char* wdev = nullptr;               // dtype weights
@@ -130,7 +132,7 @@ struct mbr_core {
   void* XH = nullptr;
   float* gates = nullptr;
   void* U = nullptr;
-  void *qt = nullptr, *kt = nullptr, *vtt = nullptr, *qb = nullptr, *kb = nullptr, *vtb = nullptr;
+  void *qt = nullptr, *kt = nullptr, *vt = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
   void* O = nullptr;
   void* H1 = nullptr;
   void* H2 = nullptr;
@@ -178,10 +180,11 @@ int setup_tables_and_groups(mbr_core* c) {
   // grouped GEMM descriptors
   std::vector<GemmGroup> groups;
   std::vector<GemmTile> tiles;
-  const int MT = (c->Bmax * c->T + 127) / 128;  // row tiles for the largest batch
+  const int TM = c->tile_m;
+  const int MT = (c->Bmax * c->T + TM - 1) / TM;  // row tiles for the largest batch
   auto add_tiles = [&](int group, int N) {
     for (int m = 0; m < MT; ++m)
-      for (int n = 0; n < (N + 127) / 128; ++n) tiles.push_back({group, m * 128, n * 128, 0});
+      for (int n = 0; n < (N + 127) / 128; ++n) tiles.push_back({group, m * TM, n * 128, 0});
   };
   c->g_embed = 0;
   c->t_embed = 0;
@@ -337,7 +340,7 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
     tw.gout = fp.append(gout);
   }
   // mask head: per stem, per layer, bands in order; the last layer's value and gate rows
-  // interleaved in blocks of 16 features so a GLU pair lands in one lane
+  // interleaved in blocks of glu_blk features so a GLU pair lands in one lane
   const int nl = cfg.mask_depth + 1;
   c->mw.resize(cfg.num_stems);
   for (int s = 0; s < cfg.num_stems; ++s) {
@@ -352,18 +355,18 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
           m.wband[j][i] = pk.append(w);
           m.bband[j][i] = fp.append(b);
         } else {
-          const int Wi = bd.width[i], wp = c->wp[i];
+          const int Wi = bd.width[i], wp = c->wp[i], P = c->glu_blk;
           std::vector<double> r((size_t)2 * wp * MH, 0.0), rb((size_t)2 * wp, 0.0);
-          for (int q = 0; q < wp / 16; ++q)
-            for (int k = 0; k < 16; ++k) {
-              const int e = 16 * q + k;
+          for (int q = 0; q < wp / P; ++q)
+            for (int k = 0; k < P; ++k) {
+              const int e = P * q + k;
               if (e >= Wi) continue;
               for (int x = 0; x < MH; ++x) {
-                r[(size_t)(32 * q + k) * MH + x] = w[(size_t)e * MH + x];
-                r[(size_t)(32 * q + 16 + k) * MH + x] = w[(size_t)(Wi + e) * MH + x];
+                r[(size_t)(2 * P * q + k) * MH + x] = w[(size_t)e * MH + x];
+                r[(size_t)(2 * P * q + P + k) * MH + x] = w[(size_t)(Wi + e) * MH + x];
               }
-              rb[32 * q + k] = b[e];
-              rb[32 * q + 16 + k] = b[Wi + e];
+              rb[2 * P * q + k] = b[e];
+              rb[2 * P * q + P + k] = b[Wi + e];
             }
           m.wband[j][i] = pk.append(r);
           m.bband[j][i] = fp.append(rb);
@@ -407,10 +410,10 @@ int alloc_workspace(mbr_core* c) {
   c->U = b + oU;
   c->qt = b + oqt;
   c->kt = b + okt;
-  c->vtt = b + ovt;
+  c->vt = b + ovt;
   c->qb = b + oqb;
   c->kb = b + okb;
-  c->vtb = b + ovb;
+  c->vb = b + ovb;
   c->O = b + oO;
   c->H1 = b + oH1;
   c->H2 = b + oH2;
@@ -444,6 +447,10 @@ struct Prof {
     if (prof) { int r_ = prof->end(); if (r_) return r_; } \
   } while (0)
 
+hipError_t gemm(const GemmLaunch& L, hipStream_t s) {
+  return L.dtype == DT_F32 ? launch_gemm(L, s) : launch_gemm2(L, s);
+}
+
 int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t s, int stop_stage,
                 Prof* prof = nullptr) {
   const mbr_config& cfg = c->cfg;
@@ -470,7 +477,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   ge.groups = c->groups;
   ge.tiles = c->tiles + c->t_embed;
   ge.n_tiles = c->n_embed;
-  LAUNCH(MBR_K_EMBED, launch_gemm(ge, s));
+  LAUNCH(MBR_K_EMBED, gemm(ge, s));
 
   NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
   LAUNCH(MBR_K_NORM, launch_norm(nl, s));
@@ -494,7 +501,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     QkvArgs& qa = gq.qkv;
     qa.q = axis ? c->qb : c->qt;
     qa.k = axis ? c->kb : c->kt;
-    qa.vt = axis ? c->vtb : c->vtt;
+    qa.v = axis ? c->vb : c->vt;
     qa.cos = axis ? c->cos_b : c->cos_t;
     qa.sin = axis ? c->sin_b : c->sin_t;
     qa.axis = axis;
@@ -503,14 +510,14 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     qa.heads = c->H;
     qa.dh = c->DH;
     qa.npad = axis ? 64 : c->Tp;
-    LAUNCH(MBR_K_QKV, launch_gemm(gq, s));
+    LAUNCH(MBR_K_QKV, gemm(gq, s));
 
     AttnLaunch al{};
     al.dtype = dt;
     al.axis = axis;
     al.q = qa.q;
     al.k = qa.k;
-    al.vt = qa.vt;
+    al.v = qa.v;
     al.gates = c->gates;
     al.o = c->O;
     al.n = axis ? c->NB : c->T;
@@ -536,7 +543,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     go.dense.K = c->I;
     go.dense.lda = c->I;
     go.dense.ldb = c->I;
-    LAUNCH(MBR_K_OUT_PROJ, launch_gemm(go, s));
+    LAUNCH(MBR_K_OUT_PROJ, gemm(go, s));
 
     NormLaunch n0{dt, 0, c->X, c->XH, nullptr, nullptr, nullptr, nullptr, NT, c->D, c->H};
     LAUNCH(MBR_K_NORM, launch_norm(n0, s));
@@ -555,7 +562,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g1.dense.K = c->D;
     g1.dense.lda = c->D;
     g1.dense.ldb = c->D;
-    LAUNCH(MBR_K_FFN1, launch_gemm(g1, s));
+    LAUNCH(MBR_K_FFN1, gemm(g1, s));
 
     GemmLaunch g2{};
     g2.dtype = dt;
@@ -571,7 +578,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g2.dense.K = c->FF;
     g2.dense.lda = c->FF;
     g2.dense.ldb = c->FF;
-    LAUNCH(MBR_K_FFN2, launch_gemm(g2, s));
+    LAUNCH(MBR_K_FFN2, gemm(g2, s));
 
     const bool last = t == ntr - 1;
     NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
@@ -606,7 +613,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
         gm.glu_total = c->total;
         gm.glu_frames = c->T;
       }
-      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, launch_gemm(gm, s));
+      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, gemm(gm, s));
     }
   }
   if (stop_stage == 1000) return MBR_OK;
@@ -718,6 +725,8 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->Bmax = cfg->max_batch;
   c->total = c->bands.total_width();
   const int kstep = cfg->dtype == MBR_F32 ? 16 : 32;
+  c->tile_m = cfg->dtype == MBR_F32 ? 128 : gemm2_tile_rows();
+  c->glu_blk = cfg->dtype == MBR_F32 ? 16 : 32;
   c->kpad.resize(c->NB);
   c->kcol.resize(c->NB);
   c->wp.resize(c->NB);
@@ -727,7 +736,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
     c->kcol[i] = col;
     col += c->kpad[i];
     c->kpad_max = std::max(c->kpad_max, c->kpad[i]);
-    c->wp[i] = round_up(c->bands.width[i], 16);
+    c->wp[i] = round_up(c->bands.width[i], c->glu_blk);
   }
   c->kpad_total = col;
   // read the caller's weights
