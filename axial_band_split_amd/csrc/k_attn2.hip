@@ -1,0 +1,230 @@
+// Time-axis attention for 16-bit operands on gfx950 (flash form, online softmax in fp32).
+//
+// One sequence is one (batch, band) pair of the time Transformer, its positions the frames
+// ([P1] "The two transformers are not the same shape"); per head, o = softmax(q k^T) v with the
+// 1/sqrt(dh) scale already folded into W_q, times the head's gate ([P1] "Per Attention layer").
+//
+//   * workgroup = 4 waves x 32 queries; the K tile [64 keys][dh] and the V^T tile [dh][64 keys]
+//     (V^T is written that way by the q/k/v projection) arrive by 16-byte direct global->LDS loads
+//     into a 2-stage ring, the next tile in flight while the current one is consumed;
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16: a lane owns one query column and 16 of
+//     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart, and its
+//     sum none until the end;
+//   * the probabilities feed the P.V product straight from the S^T accumulators (the 8 keys a lane
+//     supplies per 16-key step are the two runs of 4 it holds; V^T is read in the same key order);
+//   * the running max used for the exponentials is raised only when a tile's max exceeds it by more
+//     than 8 (log2 units); until then the accumulators need no rescaling.  Any reference value gives
+//     the same softmax, the bound keeps every exponential <= 2^8;
+//   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by the row index, so the 32 rows one
+//     fragment read touches spread over all LDS banks;
+//   * only the last key tile is masked (keys >= n), and the workgroup order keeps all query blocks of
+//     one (sequence, head) on one XCD, whose L2 then serves its K and V.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mbr {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mma32(f32x16& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma16(const char* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+constexpr float kNegBig = -1e30f;
+constexpr float kLazy = 8.0f;   // log2 headroom before the reference max must move
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
+  constexpr int KT = 64;                     // keys per tile
+  constexpr int KROWB = DH * 2;              // bytes per K row
+  constexpr int KCH = KROWB / 16;            // 16-byte chunks per K row
+  constexpr int VROWB = KT * 2;              // bytes per V^T row (64 keys)
+  constexpr int KBYTES = KT * KROWB, VBYTES = DH * VROWB;
+  constexpr int STAGE = KBYTES + VBYTES;
+  constexpr int KLD = KBYTES / (256 * 16), VLD = VBYTES / (256 * 16);   // loads per thread per stage
+  constexpr int KSTEPS = DH / 16;            // 32x32x16 steps over dh for S
+  constexpr int DT = DH / 32;                // 32-row d tiles of O^T
+  static_assert(KLD >= 1 && VLD >= 1, "tile loader");
+  using frag = typename Frag<T>::type;
+  typedef typename Frag<T>::half_type h4;
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  // workgroup order: all query blocks of one (seq, head) on one XCD
+  const int nqb = L.npad / 128;
+  const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int logical = x * per + min(x, rem) + slot;
+  const int qb = logical % nqb, sh = logical / nqb;
+  const int seq = sh / L.heads, h = sh - seq * L.heads;
+  const int n = L.n, npad = L.npad;
+  const int q0 = qb * 128 + w * 32;
+  const size_t base = (size_t)sh * (size_t)npad * DH;
+  const char* Qg = (const char*)((const T*)L.q + base);
+  const char* Kg = (const char*)((const T*)L.k + base);
+  const char* Vg = (const char*)((const T*)L.v + base);     // V^T [DH][npad]
+
+  // this thread's DMA chunks: K slot c -> key c / KCH, physical chunk c % KCH holds logical chunk
+  // (c % KCH) ^ (key % KCH); V^T slot c -> dim c / 8, 8 keys per chunk, same permutation by dim
+  const char* ksrc[KLD];
+  int kdst[KLD];
+#pragma unroll
+  for (int j = 0; j < KLD; ++j) {
+    const int c = j * 256 + threadIdx.x;
+    const int row = c / KCH, pc = c % KCH;
+    ksrc[j] = Kg + (size_t)row * KROWB + ((pc ^ (row % KCH)) << 4);
+    kdst[j] = (j * 256 + w * 64) * 16;
+  }
+  const char* vsrc[VLD];
+  int vdst[VLD];
+#pragma unroll
+  for (int j = 0; j < VLD; ++j) {
+    const int c = j * 256 + threadIdx.x;
+    const int row = c >> 3, pc = c & 7;
+    vsrc[j] = Vg + (size_t)row * npad * 2 + ((pc ^ (row & 7)) << 4);
+    vdst[j] = KBYTES + (j * 256 + w * 64) * 16;
+  }
+  auto issue = [&](int kt) {
+    char* st = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int j = 0; j < KLD; ++j) dma16(ksrc[j] + (size_t)kt * KT * KROWB, st + kdst[j]);
+#pragma unroll
+    for (int j = 0; j < VLD; ++j) dma16(vsrc[j] + (size_t)kt * KT * 2, st + vdst[j]);
+  };
+
+  // q fragments: B operand of S^T = K Q^T; lane holds query q0 + l32, dims 16*ks + 8*g .. +7
+  frag qf[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *(const frag*)(Qg + ((size_t)(q0 + l32) * DH + 16 * ks + 8 * g) * 2);
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[d][v] = 0.f;
+  float mref = kNegBig, lsum = 0.f;
+  const float c2 = L.scale_log2;
+
+  const int ntiles = (n + KT - 1) / KT;
+  issue(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 1 < ntiles) issue(kt + 1);
+    const char* st = lds + (kt & 1) * STAGE;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[r][v] = 0.f;
+      const int row = r * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int lc = 2 * ks + g;
+        const frag a = *(const frag*)(st + row * KROWB + ((lc ^ (row % KCH)) << 4));
+        mma32(s[r], a, qf[ks]);
+      }
+    }
+    if (kt == ntiles - 1 && (n & (KT - 1))) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt * KT + r * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (key >= n) s[r][v] = kNegBig;
+        }
+    }
+    float mx = kNegBig;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[r][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    if (__any(mx > mref + kLazy)) {
+      const float mnew = fmaxf(mref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[r][v] * c2 - mref);
+        s[r][v] = p;
+        part += p;
+      }
+    lsum += part;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = t >> 1, hv = (t & 1) * 8;
+      frag pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(s[r][hv + e]);
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const int row = d * 32 + l32;              // head dim
+        const char* vr = st + KBYTES + row * VROWB;
+        const int x7 = row & 7;
+        const h4 lo = *(const h4*)(vr + (((2 * t) ^ x7) << 4) + 8 * g);
+        const h4 hi = *(const h4*)(vr + (((2 * t + 1) ^ x7) << 4) + 8 * g);
+        frag a;
+        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+        mma32(o[d], a, pf);
+      }
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 32, 64);
+  const int q = q0 + l32;
+  if (q >= n) return;
+  const size_t row = (size_t)seq * L.frames + q;
+  const float scale = L.gates[row * L.heads + h] / lsum;
+  T* dst = (T*)L.o + row * (L.heads * DH) + h * DH;
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) {
+      h4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = cvt<T>(o[d][4 * b4 + e] * scale);
+      *(h4*)(dst + d * 32 + 8 * b4 + 4 * g) = out;
+    }
+}
+
+template <typename T>
+hipError_t launch_t(const AttnLaunch& L, hipStream_t stream) {
+  dim3 grid((L.npad / 128) * L.heads * L.seqs), block(256);
+  if (L.dh == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 64>), grid, block, 0, stream, L);
+  else if (L.dh == 32) hipLaunchKernelGGL((attn_time2_kernel<T, 32>), grid, block, 0, stream, L);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream) {
+  if (L.npad % 128 || L.axis != 0) return hipErrorInvalidValue;
+  switch (L.dtype) {
+    case DT_F16: return launch_t<f16>(L, stream);
+    case DT_BF16: return launch_t<bf16>(L, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mbr

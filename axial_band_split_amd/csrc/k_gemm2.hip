@@ -211,6 +211,24 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(GemmLaunch L) {
         h = f / qa.dh;
         d0 = f - h * qa.dh;
       }
+      if constexpr (EPI == EPI_QKV) {
+        if (which == 2 && qa.axis == 0) {
+          // time axis: v goes out transposed, [seq][h][dh][npad]; lane = row, so every store
+          // instruction writes 64 consecutive positions of one head dimension
+          const int row = rbase + lane;
+          if (row < M) {
+            const int seq = row / qa.frames, pos = row - seq * qa.frames;
+            T* vt = (T*)qa.v + (size_t)seq * qa.heads * qa.dh * qa.npad + pos;
+            const int f0 = cbase - 2 * qa.heads * qa.dh;   // v feature of this wave's first column
+#pragma unroll 8
+            for (int d = 0; d < 64; ++d) {
+              // feature f = h * dh + dd sits at row (h * dh + dd) of the [H*dh][npad] block of seq
+              vt[(size_t)(f0 + d) * qa.npad] = cvt<T>(ep[lane * EP_STRIDE + d]);
+            }
+          }
+          continue;
+        }
+      }
 #pragma unroll 2
       for (int it = 0; it < 8; ++it) {
         const int r = it * 8 + (lane >> 3);

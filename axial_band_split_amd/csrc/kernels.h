@@ -115,6 +115,9 @@ struct AttnLaunch {
   float scale_log2;         // dh^-1/2 * log2(e) when the scale is not folded; 1*log2(e) otherwise
 };
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t stream);
+// Time axis, 16-bit operands: v must be V^T [seqs][H][dh][npad] (the 16-bit q/k/v projection writes
+// it that way for the time axis); npad % 128 == 0.
+hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream);
 
 // Inverse-index average of the GLU output M [stems][B][ΣW][T] into the masks.
 struct AverageLaunch {

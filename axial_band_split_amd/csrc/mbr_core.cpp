@@ -528,7 +528,8 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     al.frames = c->T;
     al.batch = batch;
     al.scale_log2 = 1.4426950408889634f;  // the 1/sqrt(dh) scale is folded into W_q
-    LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME, launch_attention(al, s));
+    LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME,
+           (axis == 0 && dt != MBR_F32) ? launch_attention_time2(al, s) : launch_attention(al, s));
 
     GemmLaunch go{};
     go.dtype = dt;
