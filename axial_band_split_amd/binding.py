@@ -33,6 +33,10 @@ _SIGS = {
     "mbr_core_forward_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
                                             C.POINTER(C.c_double), C.POINTER(C.c_int32)]),
     "mbr_core_device_bytes": (C.c_int64, [C.c_void_p]),
+    "mbr_k_gemm": (C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                             C.c_int, C.c_int, C.c_void_p]),
+    "mbr_k_gemm_variants": (C.c_int, []),
+    "mbr_k_gelu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]),
 }
 KERNEL_KINDS = ("gather", "embed", "norm", "qkv", "attn_time", "attn_band", "out_proj", "ffn1", "ffn2",
                 "mask_hidden", "mask_glu", "average")
@@ -155,6 +159,20 @@ def mbr_core_forward_profiled(h, stft_repr_ptr: int, masks_ptr: int, batch: int,
 
 def mbr_core_device_bytes(h) -> int:
     return lib().mbr_core_device_bytes(h)
+
+
+def mbr_k_gemm(dtype: int, a_ptr: int, b_ptr: int, bias_ptr: int, c_ptr: int, M: int, N: int, K: int, variant: int = 0,
+               out16: bool = False, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_k_gemm(dtype, C.c_void_p(a_ptr), C.c_void_p(b_ptr), C.c_void_p(bias_ptr or None),
+                            C.c_void_p(c_ptr), M, N, K, variant, int(out16), C.c_void_p(stream_ptr)))
+
+
+def mbr_k_gelu(x_ptr: int, y_ptr: int, n: int, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_k_gelu(C.c_void_p(x_ptr), C.c_void_p(y_ptr), n, C.c_void_p(stream_ptr)))
+
+
+def mbr_k_gemm_variants() -> int:
+    return lib().mbr_k_gemm_variants()
 
 
 # ----------------------------------------------------------------------------- marshalling helpers

@@ -65,8 +65,82 @@ __global__ __launch_bounds__(256) void norm_kernel(NormLaunch L) {
   }
 }
 
+// The same passes for D a multiple of 128: 32 lanes per row (two rows per wave), 16-byte loads
+// and stores, reductions over the 32 lanes of the row.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void norm4_kernel(NormLaunch L) {
+  typedef typename Vec4<T>::type h4;
+  const int lane = threadIdx.x & 63, l = lane & 31;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool valid = row < L.rows;
+  const int D = L.D, D4 = D >> 2;
+  float4* x4 = (float4*)L.x + (size_t)(valid ? row : 0) * D4;
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    v[j] = valid ? x4[l + 32 * j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float sqrtD = sqrtf((float)D);
+  if (L.mode != 0) {
+    const float inv = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+    const float4* g4 = (const float4*)L.gain;
+    ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const float4 gg = g4[l + 32 * j];
+      v[j] = make_float4(v[j].x * inv * gg.x, v[j].y * inv * gg.y, v[j].z * inv * gg.z, v[j].w * inv * gg.w);
+      if (valid) x4[l + 32 * j] = v[j];
+      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  }
+  h4* xh = (h4*)((T*)L.xh + (size_t)(valid ? row : 0) * D);
+  const float k = L.mode == 2 ? 1.0f : sqrtD / fmaxf(sqrtf(ss), kNormEps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    v[j] = make_float4(v[j].x * k, v[j].y * k, v[j].z * k, v[j].w * k);
+    h4 o;
+    o[0] = cvt<T>(v[j].x); o[1] = cvt<T>(v[j].y); o[2] = cvt<T>(v[j].z); o[3] = cvt<T>(v[j].w);
+    if (valid) xh[l + 32 * j] = o;
+  }
+  if (L.mode != 2 && L.gates) {
+    for (int h = 0; h < L.H; ++h) {
+      const float4* w4 = (const float4*)(L.wg + (size_t)h * D);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const float4 ww = w4[l + 32 * j];
+        a += v[j].x * ww.x + v[j].y * ww.y + v[j].z * ww.z + v[j].w * ww.w;
+      }
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+      if (valid && l == 0) L.gates[(size_t)row * L.H + h] = sigmoidf_(a + L.bg[h]);
+    }
+  }
+}
+
 template <typename T>
 hipError_t norm_t(const NormLaunch& L, hipStream_t stream) {
+  if (L.D % 128 == 0) {
+    dim3 grid((L.rows + 7) / 8), block(256);
+    switch (L.D / 128) {
+      case 1: hipLaunchKernelGGL((norm4_kernel<T, 1>), grid, block, 0, stream, L); break;
+      case 2: hipLaunchKernelGGL((norm4_kernel<T, 2>), grid, block, 0, stream, L); break;
+      case 3: hipLaunchKernelGGL((norm4_kernel<T, 3>), grid, block, 0, stream, L); break;
+      case 4: hipLaunchKernelGGL((norm4_kernel<T, 4>), grid, block, 0, stream, L); break;
+      case 5: hipLaunchKernelGGL((norm4_kernel<T, 5>), grid, block, 0, stream, L); break;
+      case 6: hipLaunchKernelGGL((norm4_kernel<T, 6>), grid, block, 0, stream, L); break;
+      case 7: hipLaunchKernelGGL((norm4_kernel<T, 7>), grid, block, 0, stream, L); break;
+      case 8: hipLaunchKernelGGL((norm4_kernel<T, 8>), grid, block, 0, stream, L); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((L.rows + 3) / 4), block(256);
   switch (L.D / 64) {
     case 1: hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, stream, L); break;
@@ -186,7 +260,18 @@ __global__ __launch_bounds__(256) void average_kernel(AverageLaunch L) {
   }
 }
 
+__global__ __launch_bounds__(256) void gelu_kernel(const float* x, float* y, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = gelu_erf(x[i]);
+}
+
 }  // namespace
+
+hipError_t launch_gelu(const float* x, float* y, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gelu_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_norm(const NormLaunch& L, hipStream_t stream) {
   if (L.rows <= 0) return hipSuccess;

@@ -24,6 +24,12 @@ template <> struct Frag<f16> { typedef f16x8 type; typedef f16x4 half_type; stat
 template <> struct Frag<bf16> { typedef bf16x8 type; typedef bf16x4 half_type; static constexpr int EPF = 8; };
 template <> struct Frag<float> { typedef f32x4 type; typedef float half_type; static constexpr int EPF = 4; };
 
+// Four elements of T in one vector register group (8 or 16 bytes).
+template <typename T> struct Vec4;
+template <> struct Vec4<f16> { typedef f16x4 type; };
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
 __device__ __forceinline__ void mma(f32x4& c, const f16x8& a, const f16x8& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -50,7 +56,22 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0, with
+// |error| <= 1.5e-7; odd in z.  One reciprocal, five FMAs and one exponential.
+__device__ __forceinline__ float erf_as(float x) {
+  const float z = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  return copysignf(fmaf(-p, e, 1.0f), x);
+}
+// GELU with the error function (x * Phi(x)), as the feed-forward of the core uses it.
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 
 constexpr float kNormEps = 1e-12f;
 

@@ -33,6 +33,7 @@ enum Epi {
   EPI_RESID = 3,     // C(float) += acc (+ bias)                      (out-proj, FFN2)
   EPI_TANH = 4,      // C(T) = tanh(acc + bias)                       (mask MLP hidden layers)
   EPI_GLU = 5,       // paired value/gate column blocks -> value*sigmoid(gate), feature-major float
+  EPI_STORE16 = 6,   // C(T) = acc + bias                             (16-bit kernel; test surface)
 };
 
 struct QkvArgs {
@@ -67,10 +68,13 @@ struct GemmLaunch {
 
 // Generic 128 x 128 tile kernel (every dtype; the fp32 path uses it).  GLU pairs 16-column blocks.
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t stream);
-// 16-bit operand kernel (fp16 / bf16): 256 x 128 tiles; needs N % 64 == 0 and K % 32 == 0 for dense
-// launches; grouped tile tables must use 256-row tiles.  GLU pairs 32-column blocks.
-hipError_t launch_gemm2(const GemmLaunch& L, hipStream_t stream);
-int gemm2_tile_rows();
+// 16-bit operand kernel (fp16 / bf16) in several tile configurations (`variant`, see k_gemm2.hip);
+// needs N % 64 == 0 and K % 32 == 0; grouped tile tables must use the variant's tile rows and
+// columns.  GLU pairs 32-column blocks.
+hipError_t launch_gemm2(const GemmLaunch& L, int variant, hipStream_t stream);
+int gemm2_variants();
+int gemm2_tile_rows(int variant);
+int gemm2_tile_cols(int variant);
 
 // Row RMS norm passes over the fp32 residual stream x [rows, D].
 //   mode 0: xh = T(x * sqrt(D) / max(|x|, eps)); gates (optional) from the same normalised row
@@ -118,6 +122,9 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t stream);
 // Time axis, 16-bit operands: v must be V^T [seqs][H][dh][npad] (the 16-bit q/k/v projection writes
 // it that way for the time axis); npad % 128 == 0.
 hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream);
+
+// y = gelu(x) elementwise with the device GELU of the feed-forward epilogues (test surface).
+hipError_t launch_gelu(const float* x, float* y, int n, hipStream_t stream);
 
 // Inverse-index average of the GLU output M [stems][B][ΣW][T] into the masks.
 struct AverageLaunch {

@@ -116,7 +116,8 @@ struct mbr_core {
   int device = 0;
   int NB = 0, D = 0, H = 0, DH = 0, I = 0, FF = 0, MH = 0, T = 0, Tp = 0, Bmax = 0, total = 0;
   std::vector<int> kpad, kcol, wp;    // per band: padded K of the embedding, U column block, mask N/2
-  int tile_m = 128;                   // row tile of the grouped GEMM tables (kernel-dependent)
+  // 16-bit GEMM tile configuration per launch kind (k_gemm2.hip variants)
+  int v_embed = 0, v_qkv = 0, v_out = 0, v_ffn1 = 0, v_ffn2 = 0, v_mask = 0, v_glu = 0;
   int glu_blk = 16;                   // value / gate pairing block of the last mask layer
   int kpad_total = 0, kpad_max = 0;
   // device memory
@@ -180,11 +181,12 @@ int setup_tables_and_groups(mbr_core* c) {
   // grouped GEMM descriptors
   std::vector<GemmGroup> groups;
   std::vector<GemmTile> tiles;
-  const int TM = c->tile_m;
-  const int MT = (c->Bmax * c->T + TM - 1) / TM;  // row tiles for the largest batch
-  auto add_tiles = [&](int group, int N) {
+  const bool f32 = cfg.dtype == MBR_F32;
+  auto add_tiles = [&](int group, int N, int variant) {
+    const int TM = f32 ? 128 : gemm2_tile_rows(variant), TN = f32 ? 128 : gemm2_tile_cols(variant);
+    const int MT = (c->Bmax * c->T + TM - 1) / TM;  // row tiles for the largest batch
     for (int m = 0; m < MT; ++m)
-      for (int n = 0; n < (N + 127) / 128; ++n) tiles.push_back({group, m * TM, n * 128, 0});
+      for (int n = 0; n < (N + TN - 1) / TN; ++n) tiles.push_back({group, m * TM, n * TN, 0});
   };
   c->g_embed = 0;
   c->t_embed = 0;
@@ -201,7 +203,7 @@ int setup_tables_and_groups(mbr_core* c) {
     g.lda = c->kpad[i];
     g.ldb = c->kpad[i];
     groups.push_back(g);
-    add_tiles((int)groups.size() - 1, g.N);
+    add_tiles((int)groups.size() - 1, g.N, c->v_embed);
   }
   c->n_embed = (int)tiles.size();
   const int nl = cfg.mask_depth + 1;
@@ -234,7 +236,7 @@ int setup_tables_and_groups(mbr_core* c) {
           g.e1 = bd.width[i];
         }
         groups.push_back(g);
-        add_tiles((int)groups.size() - 1, g.N);
+        add_tiles((int)groups.size() - 1, g.N, j < nl - 1 ? c->v_mask : c->v_glu);
       }
       c->n_mask[s][j] = (int)tiles.size() - c->t_mask[s][j];
     }
@@ -447,8 +449,8 @@ struct Prof {
     if (prof) { int r_ = prof->end(); if (r_) return r_; } \
   } while (0)
 
-hipError_t gemm(const GemmLaunch& L, hipStream_t s) {
-  return L.dtype == DT_F32 ? launch_gemm(L, s) : launch_gemm2(L, s);
+hipError_t gemm(const GemmLaunch& L, int variant, hipStream_t s) {
+  return L.dtype == DT_F32 ? launch_gemm(L, s) : launch_gemm2(L, variant, s);
 }
 
 int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t s, int stop_stage,
@@ -477,7 +479,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   ge.groups = c->groups;
   ge.tiles = c->tiles + c->t_embed;
   ge.n_tiles = c->n_embed;
-  LAUNCH(MBR_K_EMBED, gemm(ge, s));
+  LAUNCH(MBR_K_EMBED, gemm(ge, c->v_embed, s));
 
   NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
   LAUNCH(MBR_K_NORM, launch_norm(nl, s));
@@ -510,7 +512,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     qa.heads = c->H;
     qa.dh = c->DH;
     qa.npad = axis ? 64 : c->Tp;
-    LAUNCH(MBR_K_QKV, gemm(gq, s));
+    LAUNCH(MBR_K_QKV, gemm(gq, c->v_qkv, s));
 
     AttnLaunch al{};
     al.dtype = dt;
@@ -544,7 +546,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     go.dense.K = c->I;
     go.dense.lda = c->I;
     go.dense.ldb = c->I;
-    LAUNCH(MBR_K_OUT_PROJ, gemm(go, s));
+    LAUNCH(MBR_K_OUT_PROJ, gemm(go, c->v_out, s));
 
     NormLaunch n0{dt, 0, c->X, c->XH, nullptr, nullptr, nullptr, nullptr, NT, c->D, c->H};
     LAUNCH(MBR_K_NORM, launch_norm(n0, s));
@@ -563,7 +565,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g1.dense.K = c->D;
     g1.dense.lda = c->D;
     g1.dense.ldb = c->D;
-    LAUNCH(MBR_K_FFN1, gemm(g1, s));
+    LAUNCH(MBR_K_FFN1, gemm(g1, c->v_ffn1, s));
 
     GemmLaunch g2{};
     g2.dtype = dt;
@@ -579,7 +581,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g2.dense.K = c->FF;
     g2.dense.lda = c->FF;
     g2.dense.ldb = c->FF;
-    LAUNCH(MBR_K_FFN2, gemm(g2, s));
+    LAUNCH(MBR_K_FFN2, gemm(g2, c->v_ffn2, s));
 
     const bool last = t == ntr - 1;
     NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
@@ -614,7 +616,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
         gm.glu_total = c->total;
         gm.glu_frames = c->T;
       }
-      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, gemm(gm, s));
+      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, gemm(gm, j < nlay - 1 ? c->v_mask : c->v_glu, s));
     }
   }
   if (stop_stage == 1000) return MBR_OK;
@@ -726,8 +728,16 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->Bmax = cfg->max_batch;
   c->total = c->bands.total_width();
   const int kstep = cfg->dtype == MBR_F32 ? 16 : 32;
-  c->tile_m = cfg->dtype == MBR_F32 ? 128 : gemm2_tile_rows();
   c->glu_blk = cfg->dtype == MBR_F32 ? 16 : 32;
+  // tile configurations of the 16-bit GEMM per launch kind, from a sweep on MI355X at the core's
+  // shapes: 256 x 128 tiles of 64 x 64 waves where N = D is small, 256 x 256 for the wide products
+  c->v_qkv = 4;
+  c->v_ffn1 = 4;
+  c->v_ffn2 = 4;
+  c->v_out = 4;
+  c->v_mask = 4;
+  c->v_glu = 4;
+  c->v_embed = 4;
   c->kpad.resize(c->NB);
   c->kcol.resize(c->NB);
   c->wp.resize(c->NB);
@@ -821,6 +831,39 @@ int mbr_core_forward_profiled(mbr_core* c, const float* in, float* out, int batc
   }
   if (rc) return rc;
   if (e != hipSuccess) return fail(MBR_E_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+  return MBR_OK;
+}
+
+int mbr_k_gemm_variants(void) { return gemm2_variants(); }
+
+int mbr_k_gelu(const float* x, float* y, int n, hipStream_t stream) {
+  if (!x || !y || n < 0) return fail(MBR_E_ARG, "bad argument");
+  HIP_TRY(launch_gelu(x, y, n, stream));
+  return MBR_OK;
+}
+
+int mbr_k_gemm(int dtype, const void* a, const void* b, const float* bias, void* cmat, int M, int N, int K,
+               int variant, int out16, hipStream_t stream) {
+  if (!a || !b || !cmat) return fail(MBR_E_ARG, "NULL argument");
+  if (M < 1 || N < 1 || K < 1 || N % 64 || K % (dtype == MBR_F32 ? 16 : 32))
+    return fail(MBR_E_ARG, "mbr_k_gemm needs N % 64 == 0 and K a multiple of the K step");
+  if (dtype != MBR_F32 && (variant < 0 || variant >= gemm2_variants())) return fail(MBR_E_ARG, "unknown variant");
+  if (dtype != MBR_F32 && dtype != MBR_F16 && dtype != MBR_BF16) return fail(MBR_E_ARG, "unknown dtype");
+  GemmLaunch L{};
+  if (out16 && dtype == MBR_F32) return fail(MBR_E_ARG, "16-bit output needs a 16-bit dtype");
+  L.dtype = dtype;
+  L.epi = out16 ? EPI_STORE16 : EPI_EMBED;
+  L.A = a;
+  L.B = b;
+  L.C = cmat;
+  L.bias = bias;
+  L.ldc = N;
+  L.M = M;
+  L.dense.N = N;
+  L.dense.K = K;
+  L.dense.lda = K;
+  L.dense.ldb = K;
+  HIP_TRY(gemm(L, variant, stream));
   return MBR_OK;
 }
 

@@ -199,6 +199,25 @@ enum {
 int mbr_core_forward_profiled(mbr_core* core, const float* stft_repr_dev, float* masks_dev, int batch,
                               hipStream_t stream, double* ms_per_kind, int32_t* launches_per_kind);
 
+/* ---- kernel test surface ------------------------------------------------------------ */
+/*
+ * One dense GEMM through the library's matrix-core kernels, for tests and tile tuning:
+ * C = A . B^T (+ bias), A [M, K] and B [N, K] row-major device arrays in `dtype` (MBR_F16 /
+ * MBR_BF16 bit patterns or float32), bias [N] float32 device array or NULL, C [M, N] device array
+ * (overwritten) in float32, or in `dtype` when out16 != 0 (16-bit dtypes only).  Needs N % 64 == 0
+ * and K % 32 == 0 (K % 16 for MBR_F32).  `variant` picks a tile configuration of the 16-bit
+ * kernel, 0 .. mbr_k_gemm_variants() - 1 (ignored for MBR_F32).  Asynchronous on `stream`.
+ */
+int mbr_k_gemm(int dtype, const void* a_dev, const void* b_dev, const float* bias_dev, void* c_dev, int M, int N,
+               int K, int variant, int out16, hipStream_t stream);
+int mbr_k_gemm_variants(void);
+/*
+ * y[i] = GELU(x[i]) = x * Phi(x) with the library's device error function (Abramowitz & Stegun
+ * 7.1.26, |erf error| <= 1.5e-7), the one the feed-forward epilogues use.  x, y: n float32 device
+ * values.  Asynchronous on `stream`.
+ */
+int mbr_k_gelu(const float* x_dev, float* y_dev, int n, hipStream_t stream);
+
 /* Device bytes held by the core (weights + workspace). */
 int64_t mbr_core_device_bytes(const mbr_core* core);
 
