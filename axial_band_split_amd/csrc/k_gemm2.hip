@@ -193,6 +193,16 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
   float* ep = (float*)(smem + w * C::EP_WAVE);
   const float* bias = L.bias ? L.bias + g.bias_off : nullptr;
   constexpr int ES = C::EP_STRIDE;
+  // global row of a local row (grouped EMBED / TANH launches: group e0's rows start at e0 * M)
+  const int64_t grow0 = (L.tiles && (EPI == EPI_EMBED || EPI == EPI_TANH)) ? (int64_t)g.e0 * M : 0;
+  // sum of a row's partial sums of squares (kSsStride slots, the unused ones stay zero): four
+  // independent 16-byte loads
+  auto row_ss = [&](const float* base, int64_t grow) -> float {
+    const float4* p = (const float4*)(base + grow * kSsStride);
+    const float4 a = p[0], b = p[1], c = p[2], d = p[3];
+    return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w)) + ((c.x + c.y) + (c.z + c.w)) +
+           ((d.x + d.y) + (d.z + d.w));
+  };
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     // stage rows i*32 .. i*32+31 of this wave's tile
@@ -201,25 +211,66 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) ep[(8 * (v >> 2) + 4 * khalf + (v & 3)) * ES + j * 32 + r32] = acc[i][j][v];
     const int rbase = m0 + wm * C::WROWS + i * 32;
+    // per-row factors of this pass, computed once by lane r%32 for row rbase + r%32 and read by
+    // the lanes that need them through a shuffle: the consumer row scale, and the producer-side
+    // normalisation of the residual read
+    float sc_mine = 1.0f, si_mine = 1.0f;
+    {
+      const int myrow = rbase + r32;
+      if (myrow < M) {
+        if (L.rowss) sc_mine = L.rs_mul / fmaxf(sqrtf(row_ss(L.rowss, grow0 + myrow)), kNormEps);
+        if (L.in_ss) si_mine = 1.0f / fmaxf(sqrtf(row_ss(L.in_ss, grow0 + myrow)), kNormEps);
+      }
+    }
     if constexpr (EPI == EPI_RESID || EPI == EPI_EMBED) {
       // fp32 rows of 64 columns: 16 lanes x 4 floats per row, 4 rows per pass
       const int c4 = (lane & 15) * 4;
       float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
       if (bias) bv = *(const float4*)(bias + cbase + c4);
+      float4 ing = make_float4(1.f, 1.f, 1.f, 1.f), xg = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (L.in_gain) ing = *(const float4*)(L.in_gain + cbase + c4);
+      if (L.xh_gain) {
+        const float4 t4 = *(const float4*)(L.xh_gain + cbase + c4);
+        xg = make_float4(t4.x * L.xh_gmul, t4.y * L.xh_gmul, t4.z * L.xh_gmul, t4.w * L.xh_gmul);
+      }
       float* Cp = (float*)L.C + g.c_off0 + g.c_offb * (int64_t)M;
-#pragma unroll 4
+#pragma unroll 2
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int row = rbase + r;
-        if (row >= M) continue;
+        const bool active = row < M;           // uniform over the 16 lanes of a row
         const float4 a = *(const float4*)(ep + r * ES + c4);
         float4* o = (float4*)(Cp + (int64_t)row * L.ldc + cbase + c4);
         float4 val = make_float4(a.x + bv.x, a.y + bv.y, a.z + bv.z, a.w + bv.w);
+        const float si = __shfl(si_mine, r, 64);
         if constexpr (EPI == EPI_RESID) {
-          const float4 xo = *o;
+          float4 xo = active ? *o : make_float4(0.f, 0.f, 0.f, 0.f);
+          if (L.in_ss) xo = make_float4(xo.x * ing.x * si, xo.y * ing.y * si, xo.z * ing.z * si, xo.w * ing.w * si);
           val = make_float4(xo.x + val.x, xo.y + val.y, xo.z + val.z, xo.w + val.w);
         }
-        *o = val;
+        if (active) *o = val;
+        const float4 hv = make_float4(val.x * xg.x, val.y * xg.y, val.z * xg.z, val.w * xg.w);
+        if (L.xh && active) {
+          typename Vec4<T>::type h4;
+          h4[0] = cvt<T>(hv.x); h4[1] = cvt<T>(hv.y); h4[2] = cvt<T>(hv.z); h4[3] = cvt<T>(hv.w);
+          *(typename Vec4<T>::type*)((T*)L.xh + (grow0 + row) * L.ldc + cbase + c4) = h4;
+        }
+        if (L.ss1) {
+          float q1 = val.x * val.x + val.y * val.y + val.z * val.z + val.w * val.w;
+          q1 += __shfl_xor(q1, 8, 64);
+          q1 += __shfl_xor(q1, 4, 64);
+          q1 += __shfl_xor(q1, 2, 64);
+          q1 += __shfl_xor(q1, 1, 64);
+          if (active && (lane & 15) == 0) L.ss1[(grow0 + row) * kSsStride + (cbase >> 6)] = q1;
+        }
+        if (L.ss2) {
+          float q2 = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+          q2 += __shfl_xor(q2, 8, 64);
+          q2 += __shfl_xor(q2, 4, 64);
+          q2 += __shfl_xor(q2, 2, 64);
+          q2 += __shfl_xor(q2, 1, 64);
+          if (active && (lane & 15) == 0) L.ss2[(grow0 + row) * kSsStride + (cbase >> 6)] = q2;
+        }
       }
     } else if constexpr (EPI == EPI_GLU) {
       // 32 value columns then their 32 gate columns; lane%32 = row, lane/32 picks 16 features
@@ -246,11 +297,12 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
         // instruction writes 32 consecutive positions of one head dimension per half wave
         const int row = rbase + r32;
         if (row < M) {
+          const float sc = sc_mine;
           const int seq = row / qa.frames, pos = row - seq * qa.frames;
           T* vt = (T*)qa.v + (size_t)seq * qa.heads * qa.dh * qa.npad + pos;
           const int f0 = cbase - 2 * qa.heads * qa.dh + khalf * 32;  // v feature h*dh + d
 #pragma unroll 8
-          for (int d = 0; d < 32; ++d) vt[(size_t)(f0 + d) * qa.npad] = cvt<T>(ep[r32 * ES + khalf * 32 + d]);
+          for (int d = 0; d < 32; ++d) vt[(size_t)(f0 + d) * qa.npad] = cvt<T>(ep[r32 * ES + khalf * 32 + d] * sc);
         }
         continue;
       }
@@ -258,9 +310,11 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
       const int c8 = (lane & 7) * 8;
       int h = 0, d0 = 0;
       if constexpr (EPI == EPI_QKV) {
-        const int f = cbase + c8 - which * qa.heads * qa.dh;
-        h = f / qa.dh;
-        d0 = f - h * qa.dh;
+        if (which < 3) {
+          const int f = cbase + c8 - which * qa.heads * qa.dh;
+          h = f / qa.dh;
+          d0 = f - h * qa.dh;
+        }
       }
       float bvals[8];
 #pragma unroll
@@ -284,6 +338,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
       for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3);
         const int row = rbase + r;
+        const float sc = __shfl(sc_mine, r, 64);
         if constexpr (EPI == EPI_QKV) {
           if (it > 0) {
             // advance the (seq, pos) pair by 8 rows
@@ -300,8 +355,21 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
         const float4 a0 = *(const float4*)(ep + r * ES + c8);
         const float4 a1 = *(const float4*)(ep + r * ES + c8 + 4);
         float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        if (L.rowss) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= sc;
+        }
         pack p;
         if constexpr (EPI == EPI_QKV) {
+          if (which == 3) {
+            // attention gates: one per head, sigmoid of the normalised row's projection + bias
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int hh = c8 + e;
+              if (hh < qa.heads) L.gates[(size_t)row * qa.heads + hh] = sigmoidf_(v[e] + L.gate_bias[hh]);
+            }
+            continue;
+          }
           if (which < 2) {
             const float4 cs = *(const float4*)(qa.cos + pos * (qa.dh >> 1) + (d0 >> 1));
             const float4 sn = *(const float4*)(qa.sin + pos * (qa.dh >> 1) + (d0 >> 1));

@@ -21,6 +21,8 @@ struct GemmGroup {
   int32_t e0, e1;           // epilogue extras (GLU: feature offset, band width)
 };
 
+constexpr int kSsStride = 16;   // floats per row of the row-statistics buffers (D <= 1024)
+
 struct GemmTile {
   int32_t group, m0, n0, pad;
 };
@@ -64,6 +66,26 @@ struct GemmLaunch {
   QkvArgs qkv;
   // GLU output layout: C[(b)][feature][t] with total features `glu_total`, frames `glu_frames`
   int32_t glu_total, glu_frames;
+  // ---- row statistics (16-bit kernel only).  Row partial sums of squares are kept per 64-column
+  // block of a D-wide row: ss[row * kSsStride + column / 64] (slots past D/64 stay zero).  For
+  // grouped launches (EMBED, TANH) the global row of a group's local row r is g.e0 * M + r.
+  // consumer side: scale row r of the product by rs_mul / max(sqrt(sum of rowss[r][*]), 1e-12)
+  const float* rowss;
+  int32_t ss_parts;
+  float rs_mul;
+  // RESID: the residual read from C is first normalised: x * in_gain[col] / max(|x|, 1e-12)
+  const float* in_ss;
+  const float* in_gain;
+  // RESID / EMBED producer side: xh[row][col] = T(x_new * xh_gain[col] * xh_gmul) (gain optional),
+  // ss1 partials of x_new^2, ss2 partials of (x_new * xh_gain * xh_gmul)^2
+  void* xh;
+  const float* xh_gain;
+  float xh_gmul;
+  float* ss1;
+  float* ss2;
+  // QKV: columns 3*H*dh .. 3*H*dh + H - 1 are the attention gates: gates[row][h] = sigmoid(. + bias)
+  float* gates;
+  const float* gate_bias;
 };
 
 // Generic 128 x 128 tile kernel (every dtype; the fp32 path uses it).  GLU pairs 16-column blocks.

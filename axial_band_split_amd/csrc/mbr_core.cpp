@@ -138,6 +138,10 @@ struct mbr_core {
   void* H1 = nullptr;
   void* H2 = nullptr;
   float* Mglu = nullptr;
+  // row partial sums of squares (16-bit path), [tokens][D/64]
+  float* ssA = nullptr;   // of the residual stream x after a feed-forward (before the output norm)
+  float* ssB = nullptr;   // of x * gamma_out: the next attention's normalised input
+  float* ssC = nullptr;   // of x after the attention residual: the feed-forward's normalised input
   // tables
   int32_t* band_info = nullptr;
   int32_t* gather_pair = nullptr;
@@ -202,6 +206,7 @@ int setup_tables_and_groups(mbr_core* c) {
     g.K = c->kpad[i];
     g.lda = c->kpad[i];
     g.ldb = c->kpad[i];
+    g.e0 = i;          // global rows of this band start at i * (batch * frames)
     groups.push_back(g);
     add_tiles((int)groups.size() - 1, g.N, c->v_embed);
   }
@@ -228,6 +233,7 @@ int setup_tables_and_groups(mbr_core* c) {
           g.N = c->MH;
           g.c_off0 = 0;
           g.c_offb = (int64_t)i * c->MH;
+          g.e0 = i;
         } else {
           g.N = 2 * c->wp[i];
           g.c_off0 = 0;
@@ -319,9 +325,15 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
     const auto& w2 = W[idx++];
     const auto& b2 = W[idx++];
     const auto& go = W[idx++];
-    std::vector<double> q((size_t)3 * I * D);
+    // 16-bit path: 64 more rows after q, k, v carry the gate projection (H rows, rest zero), so the
+    // gates come out of the same product
+    const int qrows = 3 * I + (cfg.dtype == MBR_F32 ? 0 : 64);
+    std::vector<double> q((size_t)qrows * D, 0.0);
     for (int o = 0; o < 3 * I; ++o)
       for (int e = 0; e < D; ++e) q[(size_t)o * D + e] = wqkv[(size_t)o * D + e] * ga[e] * (o < I ? qscale : 1.0);
+    if (cfg.dtype != MBR_F32)
+      for (int hh = 0; hh < H; ++hh)
+        for (int e = 0; e < D; ++e) q[(size_t)(3 * I + hh) * D + e] = wg[(size_t)hh * D + e] * ga[e];
     std::vector<double> g((size_t)H * D);
     for (int h = 0; h < H; ++h)
       for (int e = 0; e < D; ++e) g[(size_t)h * D + e] = wg[(size_t)h * D + e] * ga[e];
@@ -401,6 +413,7 @@ int alloc_workspace(mbr_core* c) {
          oqb = place(attn_b), okb = place(attn_b), ovb = place(attn_b), oO = place(NT * c->I * esz),
          oH1 = place(NT * std::max(c->FF, c->MH) * esz), oH2 = place(NT * c->MH * esz),
          oM = place((size_t)c->cfg.num_stems * BT * c->total * 4);
+  size_t oSA = place(NT * kSsStride * 4), oSB = place(NT * kSsStride * 4), oSC = place(NT * kSsStride * 4);
   c->ws_bytes = off;
   hipError_t e = hipMalloc(&c->ws, off);
   if (e != hipSuccess) return fail(MBR_E_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
@@ -420,6 +433,9 @@ int alloc_workspace(mbr_core* c) {
   c->H1 = b + oH1;
   c->H2 = b + oH2;
   c->Mglu = (float*)(b + oM);
+  c->ssA = (float*)(b + oSA);
+  c->ssB = (float*)(b + oSB);
+  c->ssC = (float*)(b + oSC);
   return MBR_OK;
 }
 
@@ -462,6 +478,11 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   const char* W = c->wdev;
   const size_t esz = dtype_size(dt);
   auto wptr = [&](size_t off) { return (const void*)(W + off * esz); };
+  // 16-bit path: RMSNorms become row statistics written by the producing GEMM epilogues and row
+  // scales applied by the consuming ones; the fp32 path runs explicit norm passes
+  const bool fused = dt != MBR_F32;
+  const int parts = c->D / 64;
+  const float sqrtD = std::sqrt((float)c->D);
 
   GatherLaunch gl{dt, in, c->U, c->band_info, c->gather_pair, c->NB, batch, c->T, c->bands.n_freqs,
                   c->bands.channels, cfg.io_layout, c->kpad_max};
@@ -479,10 +500,17 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   ge.groups = c->groups;
   ge.tiles = c->tiles + c->t_embed;
   ge.n_tiles = c->n_embed;
+  if (fused) {
+    ge.xh = c->XH;     // x0 in 16 bits and its row sums of squares: the first attention's input
+    ge.ss1 = c->ssB;
+    ge.ss_parts = parts;
+  }
   LAUNCH(MBR_K_EMBED, gemm(ge, c->v_embed, s));
 
-  NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
-  LAUNCH(MBR_K_NORM, launch_norm(nl, s));
+  if (!fused) {
+    NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
+    LAUNCH(MBR_K_NORM, launch_norm(nl, s));
+  }
   if (stop_stage == 0) return MBR_OK;
 
   const int ntr = 2 * cfg.depth;
@@ -496,8 +524,15 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     gq.A = c->XH;
     gq.B = wptr(tw.wqkv);
     gq.M = NT;
-    gq.dense.N = 3 * c->I;
+    gq.dense.N = 3 * c->I + (fused ? 64 : 0);
     gq.dense.K = c->D;
+    if (fused) {
+      gq.rowss = c->ssB;
+      gq.ss_parts = parts;
+      gq.rs_mul = sqrtD;
+      gq.gates = c->gates;
+      gq.gate_bias = c->fdev + tw.bg;
+    }
     gq.dense.lda = c->D;
     gq.dense.ldb = c->D;
     QkvArgs& qa = gq.qkv;
@@ -546,10 +581,21 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     go.dense.K = c->I;
     go.dense.lda = c->I;
     go.dense.ldb = c->I;
+    if (fused) {
+      if (t > 0) {       // the previous Transformer's output norm, applied as the residual is read
+        go.in_ss = c->ssA;
+        go.in_gain = c->fdev + c->tw[t - 1].gout;
+      }
+      go.xh = c->XH;     // x in 16 bits and its row sums of squares: the feed-forward's input
+      go.ss1 = c->ssC;
+      go.ss_parts = parts;
+    }
     LAUNCH(MBR_K_OUT_PROJ, gemm(go, c->v_out, s));
 
-    NormLaunch n0{dt, 0, c->X, c->XH, nullptr, nullptr, nullptr, nullptr, NT, c->D, c->H};
-    LAUNCH(MBR_K_NORM, launch_norm(n0, s));
+    if (!fused) {
+      NormLaunch n0{dt, 0, c->X, c->XH, nullptr, nullptr, nullptr, nullptr, NT, c->D, c->H};
+      LAUNCH(MBR_K_NORM, launch_norm(n0, s));
+    }
 
     GemmLaunch g1{};
     g1.dtype = dt;
@@ -565,6 +611,11 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g1.dense.K = c->D;
     g1.dense.lda = c->D;
     g1.dense.ldb = c->D;
+    if (fused) {
+      g1.rowss = c->ssC;
+      g1.ss_parts = parts;
+      g1.rs_mul = sqrtD;
+    }
     LAUNCH(MBR_K_FFN1, gemm(g1, c->v_ffn1, s));
 
     GemmLaunch g2{};
@@ -581,14 +632,32 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     g2.dense.K = c->FF;
     g2.dense.lda = c->FF;
     g2.dense.ldb = c->FF;
+    if (fused) {
+      // x (before this Transformer's output norm) stays in X; x * gamma_out goes out in 16 bits with
+      // the row sums of squares of x (ssA) and of x * gamma_out (ssB) for the consumers
+      g2.xh = c->XH;
+      g2.xh_gain = c->fdev + tw.gout;
+      g2.xh_gmul = 1.0f / sqrtD;
+      g2.ss1 = c->ssA;
+      g2.ss2 = c->ssB;
+      g2.ss_parts = parts;
+    }
     LAUNCH(MBR_K_FFN2, gemm(g2, c->v_ffn2, s));
 
     const bool last = t == ntr - 1;
-    NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
-                  last ? nullptr : c->fdev + c->tw[t + 1].wg, last ? nullptr : c->fdev + c->tw[t + 1].bg,
-                  NT, c->D, c->H};
-    LAUNCH(MBR_K_NORM, launch_norm(no, s));
-    if (stop_stage == 1 + t) return MBR_OK;
+    if (!fused) {
+      NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
+                    last ? nullptr : c->fdev + c->tw[t + 1].wg, last ? nullptr : c->fdev + c->tw[t + 1].bg,
+                    NT, c->D, c->H};
+      LAUNCH(MBR_K_NORM, launch_norm(no, s));
+    }
+    if (stop_stage == 1 + t) {
+      if (fused) {       // taps show x after the output norm
+        NormLaunch no{dt, 1, c->X, c->XH, c->fdev + tw.gout, nullptr, nullptr, nullptr, NT, c->D, c->H};
+        HIP_TRY(launch_norm(no, s));
+      }
+      return MBR_OK;
+    }
   }
 
   const int nlay = cfg.mask_depth + 1;
@@ -610,6 +679,11 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
         gm.C = dst;
         gm.ldc = c->MH;
         src = dst;
+        if (fused && j == 0) {   // the last Transformer's output norm, as a row scale
+          gm.rowss = c->ssA;
+          gm.ss_parts = parts;
+          gm.rs_mul = sqrtD;
+        }
       } else {
         gm.epi = EPI_GLU;
         gm.C = c->Mglu;
