@@ -10,12 +10,13 @@
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16: a lane owns one query column and 16 of
 //     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart, and its
 //     sum none until the end;
-//   * the probabilities feed the P.V product straight from the S^T accumulators (the 8 keys a lane
-//     supplies per 16-key step are the two runs of 4 it holds; V^T is read in the same key order);
+//   * the probabilities feed the P.V product straight from the S^T accumulators: the K rows of the
+//     S^T product are taken in a permuted order so that the 8 probabilities a lane holds for one
+//     16-key step belong to 8 consecutive keys, and the matching V^T operand is one 16-byte read;
 //   * the running max used for the exponentials is raised only when a tile's max exceeds it by more
 //     than 8 (log2 units); until then the accumulators need no rescaling.  Any reference value gives
 //     the same softmax, the bound keeps every exponential <= 2^8;
-//   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by the row index, so the 32 rows one
+//   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by (row >> 1) & 7, so the rows one
 //     fragment read touches spread over all LDS banks;
 //   * only the last key tile is masked (keys >= n), and the workgroup order keeps all query blocks of
 //     one (sequence, head) on one XCD, whose L2 then serves its K and V.
@@ -41,6 +42,13 @@ __device__ __forceinline__ void dma16(const char* g, char* lds_wave_base) {
 
 constexpr float kNegBig = -1e30f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the reference max must move
+
+// LDS rows of 128 bytes (8 chunks of 16): chunk c of row r sits in slot c ^ ((r >> 1) & 7), so any
+// 16 consecutive rows read at one chunk cover all 64 banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// Key order inside a 32-key S^T tile: the A operand row m holds key perm(m) (bits 2 and 3 swapped),
+// which puts the 8 probabilities a lane feeds to one P.V step on 8 consecutive keys.
+__device__ __forceinline__ int perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   for (int j = 0; j < KLD; ++j) {
     const int c = j * 256 + threadIdx.x;
     const int row = c / KCH, pc = c % KCH;
-    ksrc[j] = Kg + (size_t)row * KROWB + ((pc ^ (row % KCH)) << 4);
+    ksrc[j] = Kg + (size_t)row * KROWB + ((pc ^ (swz8(row) % KCH)) << 4);
     kdst[j] = (j * 256 + w * 64) * 16;
   }
   const char* vsrc[VLD];
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   for (int j = 0; j < VLD; ++j) {
     const int c = j * 256 + threadIdx.x;
     const int row = c >> 3, pc = c & 7;
-    vsrc[j] = Vg + (size_t)row * npad * 2 + ((pc ^ (row & 7)) << 4);
+    vsrc[j] = Vg + (size_t)row * npad * 2 + ((pc ^ swz8(row)) << 4);
     vdst[j] = KBYTES + (j * 256 + w * 64) * 16;
   }
   auto issue = [&](int kt) {
@@ -128,11 +136,11 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[r][v] = 0.f;
-      const int row = r * 32 + l32;
+      const int row = r * 32 + perm(l32);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int lc = 2 * ks + g;
-        const frag a = *(const frag*)(st + row * KROWB + ((lc ^ (row % KCH)) << 4));
+        const frag a = *(const frag*)(st + row * KROWB + ((lc ^ (swz8(row) % KCH)) << 4));
         mma32(s[r], a, qf[ks]);
       }
     }
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = kt * KT + r * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          const int key = kt * KT + r * 32 + perm(8 * (v >> 2) + 4 * g + (v & 3));
           if (key >= n) s[r][v] = kNegBig;
         }
     }
@@ -177,14 +185,9 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
       for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(s[r][hv + e]);
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
-        const int row = d * 32 + l32;              // head dim
-        const char* vr = st + KBYTES + row * VROWB;
-        const int x7 = row & 7;
-        const h4 lo = *(const h4*)(vr + (((2 * t) ^ x7) << 4) + 8 * g);
-        const h4 hi = *(const h4*)(vr + (((2 * t + 1) ^ x7) << 4) + 8 * g);
-        frag a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+        // V^T row (head dim) d*32 + l32, keys 16t + 8g .. +7: one 16-byte chunk
+        const int row = d * 32 + l32;
+        const frag a = *(const frag*)(st + KBYTES + row * VROWB + (((2 * t + g) ^ swz8(row)) << 4));
         mma32(o[d], a, pf);
       }
     }
