@@ -113,7 +113,7 @@ struct GemmKernel {
             const int64_t idx = coff + (int64_t)row * L.ldc + col;
             if constexpr (EPI == EPI_EMBED) {
               ((float*)L.C)[idx] = v;
-            } else if constexpr (EPI == EPI_RESID) {
+            } else if constexpr (EPI == EPI_RESID || EPI == EPI_FFN2) {
               ((float*)L.C)[idx] += v;
             } else if constexpr (EPI == EPI_GELU) {
               ((T*)L.C)[idx] = cvt<T>(gelu_erf(v));
@@ -232,6 +232,7 @@ hipError_t launch_t(const GemmLaunch& L, hipStream_t stream) {
     case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, EPI_RESID>), grid, block, 0, stream, L); break;
     case EPI_TANH: hipLaunchKernelGGL((gemm_kernel<T, EPI_TANH>), grid, block, 0, stream, L); break;
     case EPI_GLU: hipLaunchKernelGGL((gemm_kernel<T, EPI_GLU>), grid, block, 0, stream, L); break;
+    case EPI_FFN2: hipLaunchKernelGGL((gemm_kernel<T, EPI_FFN2>), grid, block, 0, stream, L); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

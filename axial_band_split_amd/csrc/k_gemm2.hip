@@ -222,7 +222,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
         if (L.in_ss) si_mine = 1.0f / fmaxf(sqrtf(row_ss(L.in_ss, grow0 + myrow)), kNormEps);
       }
     }
-    if constexpr (EPI == EPI_RESID || EPI == EPI_EMBED) {
+    if constexpr (EPI == EPI_RESID || EPI == EPI_FFN2 || EPI == EPI_EMBED) {
       // fp32 rows of 64 columns: 16 lanes x 4 floats per row, 4 rows per pass
       const int c4 = (lane & 15) * 4;
       float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
         float4* o = (float4*)(Cp + (int64_t)row * L.ldc + cbase + c4);
         float4 val = make_float4(a.x + bv.x, a.y + bv.y, a.z + bv.z, a.w + bv.w);
         const float si = __shfl(si_mine, r, 64);
-        if constexpr (EPI == EPI_RESID) {
+        if constexpr (EPI == EPI_RESID || EPI == EPI_FFN2) {
           float4 xo = active ? *o : make_float4(0.f, 0.f, 0.f, 0.f);
           if (L.in_ss) xo = make_float4(xo.x * ing.x * si, xo.y * ing.y * si, xo.z * ing.z * si, xo.w * ing.w * si);
           val = make_float4(xo.x + val.x, xo.y + val.y, xo.z + val.z, xo.w + val.w);
@@ -456,6 +456,7 @@ hipError_t launch_t(const GemmLaunch& L, int variant, hipStream_t stream) {
     case EPI_TANH: return launch_epi<T, EPI_TANH>(L, variant, stream);
     case EPI_GLU: return launch_epi<T, EPI_GLU>(L, variant, stream);
     case EPI_STORE16: return launch_epi<T, EPI_STORE16>(L, variant, stream);
+    case EPI_FFN2: return launch_epi<T, EPI_FFN2>(L, variant, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -36,6 +36,7 @@ enum Epi {
   EPI_TANH = 4,      // C(T) = tanh(acc + bias)                       (mask MLP hidden layers)
   EPI_GLU = 5,       // paired value/gate column blocks -> value*sigmoid(gate), feature-major float
   EPI_STORE16 = 6,   // C(T) = acc + bias                             (16-bit kernel; test surface)
+  EPI_FFN2 = 7,      // as EPI_RESID, for the feed-forward's second layer (its own kernel name)
 };
 
 struct QkvArgs {

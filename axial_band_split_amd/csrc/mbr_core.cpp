@@ -620,7 +620,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
 
     GemmLaunch g2{};
     g2.dtype = dt;
-    g2.epi = EPI_RESID;
+    g2.epi = EPI_FFN2;
     g2.A = c->H1;
     g2.B = wptr(tw.w2);
     g2.C = c->X;

@@ -26,12 +26,30 @@ import numpy as np  # noqa: E402
 from axial_band_split_amd import binding, roofline, synth  # noqa: E402
 
 METRIC = "core audio-seconds/sec (44.1 kHz stereo) at T=1100; attn+GEMM TFLOP/s vs peak"
+# rocprofv3 kernel-name patterns of each kernel class on the 16-bit path (epilogue template ids)
+KIND_REGEX = {"embed": r"gemm2_kernel.*Li0E", "qkv": r"gemm2_kernel.*Li1E", "ffn1": r"gemm2_kernel.*Li2E",
+              "out_proj": r"gemm2_kernel.*Li3E", "mask_hidden": r"gemm2_kernel.*Li4E",
+              "mask_glu": r"gemm2_kernel.*Li5E", "ffn2": r"gemm2_kernel.*Li7E", "attn_time": r"attn_time2",
+              "attn_band": r"attn_band", "norm": r"norm", "gather": r"gather", "average": r"average"}
 MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu")
 GEMM_ATTN_KINDS = MFMA_KINDS + ("attn_band",)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_for(workload: str, kind: str):
+    """HBM bytes per launch of a kernel class from the committed counter record, or None when there
+    is no record for it or the kernel sources changed since it was taken."""
+    from axial_band_split_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_regex") != KIND_REGEX.get(kind) or rec.get("source_sha") != profiling.source_hash():
+        return None
+    return rec["bytes_per_launch"]
 
 
 def kind_flops(s: roofline.Shape, kind: str, w: synth.Workload) -> float:
@@ -42,10 +60,10 @@ def kind_flops(s: roofline.Shape, kind: str, w: synth.Workload) -> float:
 
 
 def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
-    """The oracle on a bounded sample: the band embedding, the first layer's time and band
-    Transformers, the mask head and the average of one forward, each timed once; the forward's
-    time is embedding + depth x (time + band Transformer) + mask head + average (every layer has
-    the same shape and cost)."""
+    """The oracle on a bounded sample: the band embedding, the time and band Transformers of the
+    first layers (up to three), the mask head and the average of one forward, each timed once; the
+    forward's time is embedding + depth x (mean layer) + stems x (mask head + average), since every
+    layer has the same shape and cost."""
     from oracle import model as M
 
     cfg = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads,
@@ -53,17 +71,18 @@ def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
     tables = cfg.tables()
     wn = M.named(cfg, ws)
     spec = M.read_input(x_io, w.audio_channels, w.io_layout)
+    layers = min(w.depth, 3)
     t0 = time.perf_counter()
     x = M.band_embed(spec, cfg, wn, tables)
     t1 = time.perf_counter()
-    x = M.time_transformer(x, cfg, wn, "layer0.time.", chunk=1)
+    for i in range(layers):
+        x = M.time_transformer(x, cfg, wn, f"layer{i}.time.", chunk=1)
+        x = M.band_transformer(x, cfg, wn, f"layer{i}.band.", chunk=64)
     t2 = time.perf_counter()
-    x = M.band_transformer(x, cfg, wn, "layer0.band.", chunk=64)
-    t3 = time.perf_counter()
     m = M.mask_head(x, cfg, wn, tables, 0)
     M.average(m, tables)
-    t4 = time.perf_counter()
-    est = (t1 - t0) + w.depth * ((t2 - t1) + (t3 - t2)) + w.num_stems * (t4 - t3)
+    t3 = time.perf_counter()
+    est = (t1 - t0) + w.depth * (t2 - t1) / layers + w.num_stems * (t3 - t2)
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -72,10 +91,10 @@ def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
         pass
     cores = max(threads or 1, M._WORKERS)
     return {"value": w.audio_seconds / est, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle on {w.name}: band embedding, layer 0 time + band Transformers, "
-                       f"mask head and average timed once ({t4 - t0:.1f} s), forward estimated as "
-                       f"embed + {w.depth} x layer + mask head = {est:.1f} s"),
-            "host_cpus": os.cpu_count(), "blas_threads": threads, "seconds_sampled": t4 - t0}
+            "sample": (f"fp64 numpy oracle on {w.name}: band embedding, {layers} of {w.depth} layers (time + band "
+                       f"Transformer), mask head and average of stem 0, each timed once ({t3 - t0:.1f} s); "
+                       f"forward estimated as embed + {w.depth} x mean layer + {w.num_stems} x mask head = {est:.1f} s"),
+            "host_cpus": os.cpu_count(), "blas_threads": threads, "seconds_sampled": t3 - t0}
 
 
 def main() -> int:
@@ -150,14 +169,14 @@ def main() -> int:
     if dominant in MFMA_KINDS:
         ach = kind_flops(s, dominant, w) / (dk["avg_launch_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dominant, "achieved": ach, "peak": peak_mfma, "unit": "TFLOP/s",
-                "frac": ach / peak_mfma, "traffic": None,
+                "frac": ach / peak_mfma, "traffic": traffic_for(w.name, dominant),
                 "flops_per_launch": kind_flops(s, dominant, w), "avg_launch_ms": dk["avg_launch_ms"]}
     else:
         b = roofline.bytes_per_launch(s)
         key = {"norm": "norm_pre", "gather": "gather", "average": "average", "attn_band": "attn_band"}[dominant]
         ach = b[key] / (dk["avg_launch_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": roofline.PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / roofline.PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": b[key],
+                "frac": ach / roofline.PEAK_HBM_GBS, "traffic": traffic_for(w.name, dominant), "bytes_per_launch": b[key],
                 "avg_launch_ms": dk["avg_launch_ms"]}
     ga_ms = sum(kernels[k]["ms_per_step"] for k in GEMM_ATTN_KINDS if k in kernels)
     ga_tflops = fl["total"] / (ga_ms * 1e-3) / 1e12
