@@ -72,16 +72,21 @@ class Workload:
 
 
 WORKLOADS = {
-    "c0_tiny_fp32": Workload("c0_tiny_fp32", 44100, 256, 2, 8, 32, 1, 64, 1, 2, 32, 4, 4, 2, 1,
-                             F32, IO_FS_T_C, "normal", 0, 0),
-    "c1_small_fp16": Workload("c1_small_fp16", 44100, 2048, 2, 60, 256, 1, 384, 6, 8, 64, 4, 4, 2, 1,
-                              F16, IO_FS_T_C, "one_over_f", 0, 2),
-    "c2_8s_bf16": Workload("c2_8s_bf16", 44100, 2048, 2, 60, 801, 1, 384, 6, 8, 64, 4, 4, 2, 1,
-                           BF16, IO_SC_F_T, "one_over_f", 0, 3),
-    "c3_11s_fp16": Workload("c3_11s_fp16", 44100, 2048, 2, 60, 1100, 1, 384, 6, 8, 64, 4, 4, 2, 1,
-                            F16, IO_FS_T_C, "one_over_f", 0, 4),
-    "c4_heavy_bf16": Workload("c4_heavy_bf16", 44100, 2048, 2, 60, 1100, 4, 512, 12, 8, 64, 4, 4, 2, 1,
-                              BF16, IO_FS_T_C, "one_over_f", 0, 5),
+    # 8 bands at n_fft 256, 32 frames, D=64, one layer of 2 heads x 32: the oracle's small case
+    "tiny_fp32": Workload("tiny_fp32", 44100, 256, 2, 8, 32, 1, 64, 1, 2, 32, 4, 4, 2, 1,
+                          F32, IO_FS_T_C, "normal", 0, 0),
+    # the vocals model (60 bands, D=384, depth 6, 8 x 64 heads) at 256 frames
+    "t256_fp16": Workload("t256_fp16", 44100, 2048, 2, 60, 256, 1, 384, 6, 8, 64, 4, 4, 2, 1,
+                          F16, IO_FS_T_C, "one_over_f", 0, 2),
+    # one 8 s chunk (801 frames), input in the [B, S*2, F, T] plane layout
+    "chunk8s_bf16": Workload("chunk8s_bf16", 44100, 2048, 2, 60, 801, 1, 384, 6, 8, 64, 4, 4, 2, 1,
+                             BF16, IO_SC_F_T, "one_over_f", 0, 3),
+    # one 11 s chunk (1100 frames)
+    "chunk11s_fp16": Workload("chunk11s_fp16", 44100, 2048, 2, 60, 1100, 1, 384, 6, 8, 64, 4, 4, 2, 1,
+                              F16, IO_FS_T_C, "one_over_f", 0, 4),
+    # four 11 s chunks through a D=512, depth-12 model
+    "heavy_b4_d512_bf16": Workload("heavy_b4_d512_bf16", 44100, 2048, 2, 60, 1100, 4, 512, 12, 8, 64, 4, 4, 2, 1,
+                                   BF16, IO_FS_T_C, "one_over_f", 0, 5),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

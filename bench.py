@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the Mel-Band RoFormer core on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_11s_fp16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload chunk11s_fp16]
 
 A step is one forward of the whole core (band gather and embedding, every axial Transformer, the
 mask head, the mask average) over one batch of seeded synthetic spectra already resident in HBM.
@@ -102,7 +102,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3_11s_fp16", choices=list(synth.WORKLOADS))
+    ap.add_argument("--workload", default="chunk11s_fp16", choices=list(synth.WORKLOADS))
     ap.add_argument("--profile-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

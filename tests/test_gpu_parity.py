@@ -41,7 +41,7 @@ def gpu_forward(core: binding.Core, x_io: np.ndarray) -> np.ndarray:
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["c0_tiny_fp32", "c1_small_fp16", "c2_8s_bf16", "c3_11s_fp16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "t256_fp16", "chunk8s_bf16", "chunk11s_fp16"])
 def test_masks_match_oracle_full_size(name):
     w = synth.WORKLOADS[name]
     say(f"[parity] {name}: B={w.batch} T={w.frames} dtype={synth.DTYPE_NAMES[w.dtype]} layout={w.io_layout}")
@@ -60,8 +60,8 @@ def test_masks_match_oracle_full_size(name):
 def test_heavy_architecture_matches_oracle_at_short_length():
     """The heavy configuration's architecture (dim 512, depth 12, bf16, 4 chunks) at 96 frames,
     where the oracle is quick; the full 1100-frame run is checked by properties below."""
-    w = synth.WORKLOADS["c4_heavy_bf16"].replace(frames=96, batch=2)
-    say(f"[parity] c4 architecture at T={w.frames}, B={w.batch}")
+    w = synth.WORKLOADS["heavy_b4_d512_bf16"].replace(frames=96, batch=2)
+    say(f"[parity] heavy architecture at T={w.frames}, B={w.batch}")
     cfg, ws = build(w, max_batch=4)
     x = synth.draw_input(w)
     core = binding.Core(cfg, ws)
@@ -69,29 +69,29 @@ def test_heavy_architecture_matches_oracle_at_short_length():
     core.close()
     ref = M.forward(x, ocfg(w), ws)
     err = rel_l2(y, ref)
-    say(f"[parity] c4 short: rel L2 = {err:.3e}")
+    say(f"[parity] heavy short: rel L2 = {err:.3e}")
     assert err <= TOL[w.dtype]
 
 
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 def test_tiny_config_in_half_precision(dtype):
-    w = synth.WORKLOADS["c0_tiny_fp32"].replace(dtype=dtype)
-    say(f"[parity] c0 in {synth.DTYPE_NAMES[dtype]}")
+    w = synth.WORKLOADS["tiny_fp32"].replace(dtype=dtype)
+    say(f"[parity] tiny in {synth.DTYPE_NAMES[dtype]}")
     cfg, ws = build(w)
     x = synth.draw_input(w)
     core = binding.Core(cfg, ws)
     y = gpu_forward(core, x)
     core.close()
     err = rel_l2(y, M.forward(x, ocfg(w), ws))
-    say(f"[parity] c0 {synth.DTYPE_NAMES[dtype]}: rel L2 = {err:.3e}")
+    say(f"[parity] tiny {synth.DTYPE_NAMES[dtype]}: rel L2 = {err:.3e}")
     assert err <= TOL[dtype]
 
 
 def test_fp32_stage_taps_match_oracle():
     """Band embedding, every Transformer's output and the GLU output of the fp32 path, each
     within 1e-5 relative L2 of the oracle's intermediate (the pages' stage-by-stage nulls)."""
-    w = synth.WORKLOADS["c0_tiny_fp32"].replace(depth=2)
-    say("[taps] c0 fp32, depth 2")
+    w = synth.WORKLOADS["tiny_fp32"].replace(depth=2)
+    say("[taps] tiny fp32, depth 2")
     cfg, ws = build(w, std=0.05, gamma_std=0.3)
     x = synth.draw_input(w)
     core = binding.Core(cfg, ws)
@@ -119,8 +119,8 @@ def test_fp32_stage_taps_match_oracle():
 
 
 def test_batch_below_max_and_sc_f_t_layout():
-    w = synth.WORKLOADS["c0_tiny_fp32"].replace(batch=3, io_layout=synth.IO_SC_F_T)
-    say("[parity] c0 layout 1, max_batch 3, batches 3, 2, 1")
+    w = synth.WORKLOADS["tiny_fp32"].replace(batch=3, io_layout=synth.IO_SC_F_T)
+    say("[parity] tiny layout 1, max_batch 3, batches 3, 2, 1")
     cfg, ws = build(w)
     x = synth.input_in_layout(w, synth.draw_input(w))
     core = binding.Core(cfg, ws)
@@ -136,7 +136,7 @@ def test_silent_frames_and_a_silent_band_stay_finite():
     """A fifth of the frames zeroed and one band's bins zeroed: the 1e-12 clamp keeps every row
     finite (the pages report NaN masks from an fp16 norm here) and parity still holds."""
     for dtype in (synth.F32, synth.F16):
-        w = synth.WORKLOADS["c0_tiny_fp32"].replace(dtype=dtype)
+        w = synth.WORKLOADS["tiny_fp32"].replace(dtype=dtype)
         say(f"[edge] silent frames / band, {synth.DTYPE_NAMES[dtype]}")
         cfg, ws = build(w)
         x = synth.draw_input(w)
@@ -151,8 +151,8 @@ def test_silent_frames_and_a_silent_band_stay_finite():
 
 
 def test_forward_is_deterministic():
-    w = synth.WORKLOADS["c1_small_fp16"]
-    say("[det] c1 twice")
+    w = synth.WORKLOADS["t256_fp16"]
+    say("[det] t256 twice")
     cfg, ws = build(w)
     core = binding.Core(cfg, ws)
     xd = torch.from_numpy(synth.draw_input(w)).cuda()
@@ -166,8 +166,8 @@ def test_forward_is_deterministic():
 def test_heavy_full_size_batch_consistency():
     """The heavy configuration at full size (4 chunks of 1100 frames): finite, and each chunk's
     masks are bitwise those of a batch-1 call on that chunk (chunks never interact)."""
-    w = synth.WORKLOADS["c4_heavy_bf16"]
-    say("[c4] full size, batch 4 vs batch 1")
+    w = synth.WORKLOADS["heavy_b4_d512_bf16"]
+    say("[heavy] full size, batch 4 vs batch 1")
     cfg, ws = build(w)
     core = binding.Core(cfg, ws)
     xd = torch.from_numpy(synth.draw_input(w)).cuda()

@@ -68,14 +68,14 @@ def test_inventory_matches_oracle(name):
 
 
 def test_inventory_with_two_stems_and_deeper_mask():
-    w = synth.WORKLOADS["c0_tiny_fp32"].replace(num_stems=2, mask_depth=3)
+    w = synth.WORKLOADS["tiny_fp32"].replace(num_stems=2, mask_depth=3)
     lib_inv = binding.inventory(binding.config(w))
     ora_inv = M.inventory(_oracle_cfg(w))
     assert [s for _, s, _ in lib_inv] == [tuple(s) for _, s, _ in ora_inv]
 
 
 def test_param_count_through_the_library():
-    cfg = binding.config(synth.WORKLOADS["c3_11s_fp16"])
+    cfg = binding.config(synth.WORKLOADS["chunk11s_fp16"])
     total = sum(int(np.prod(s)) for _, s, _ in binding.inventory(cfg))
     assert total == 228202788
 
@@ -83,7 +83,7 @@ def test_param_count_through_the_library():
 @pytest.mark.parametrize("field,value", [("dim", 100), ("dim_head", 48), ("dtype", 7), ("io_layout", 3),
                                          ("num_bands", 0), ("frames", 0), ("max_batch", 0), ("n_fft", 7)])
 def test_invalid_configs_are_rejected(field, value):
-    cfg = binding.config(synth.WORKLOADS["c0_tiny_fp32"], **{field: value})
+    cfg = binding.config(synth.WORKLOADS["tiny_fp32"], **{field: value})
     with pytest.raises(binding.MbrError) as e:
         binding.mbr_core_weight_count(cfg)
     assert e.value.code == binding.MBR_E_CONFIG
@@ -92,14 +92,14 @@ def test_invalid_configs_are_rejected(field, value):
 
 def test_band_with_no_bin_is_a_config_error():
     """Too many bands for the bins: some triangle falls between two bins."""
-    cfg = binding.config(synth.WORKLOADS["c0_tiny_fp32"], n_fft=32, num_bands=40)
+    cfg = binding.config(synth.WORKLOADS["tiny_fp32"], n_fft=32, num_bands=40)
     with pytest.raises(binding.MbrError) as e:
         binding.mbr_core_table_sizes(cfg)
     assert e.value.code == binding.MBR_E_CONFIG
 
 
 def test_weight_info_index_out_of_range():
-    cfg = binding.config(synth.WORKLOADS["c0_tiny_fp32"])
+    cfg = binding.config(synth.WORKLOADS["tiny_fp32"])
     n = binding.mbr_core_weight_count(cfg)
     with pytest.raises(binding.MbrError) as e:
         binding.mbr_core_weight_info(cfg, n)

@@ -176,7 +176,7 @@ def test_query_blocked_attention_is_exact():
 
 # ----------------------------------------------------------------------------- whole-core invariants
 
-def _c0_like(**kw):
+def _tiny_like(**kw):
     base = dict(sample_rate=44100, n_fft=256, audio_channels=2, num_bands=8, dim=16, depth=1, heads=2, dim_head=8)
     base.update(kw)
     return M.CoreConfig(**base)
@@ -184,7 +184,7 @@ def _c0_like(**kw):
 
 def test_core_is_scale_invariant():
     """Every band's input is normalised first, so scaling the spectrum changes nothing."""
-    cfg = _c0_like()
+    cfg = _tiny_like()
     ws = synth.draw_weights(M.inventory(cfg), synth.F32, seed=1, std=0.2)
     x = np.random.default_rng(2).standard_normal((1, 258, 5, 2))
     assert np.allclose(M.forward(7.25 * x, cfg, ws), M.forward(x, cfg, ws), rtol=1e-11, atol=1e-13)
@@ -193,7 +193,7 @@ def test_core_is_scale_invariant():
 def test_constant_band_masks_average_to_the_constant():
     """Last mask layer zero, value bias c, gate bias 0: every band's mask is c * sigmoid(0) = c/2,
     so every averaged bin is c/2 whatever the band count."""
-    cfg = _c0_like()
+    cfg = _tiny_like()
     inv = M.inventory(cfg)
     ws = synth.draw_weights(inv, synth.F32, seed=3, std=0.2)
     c = 0.734
@@ -210,7 +210,7 @@ def test_constant_band_masks_average_to_the_constant():
 
 def test_average_equals_dense_incidence_form():
     """The index-based scatter average equals (incidence^T m) / counts built densely."""
-    cfg = _c0_like()
+    cfg = _tiny_like()
     t = cfg.tables()
     rng = np.random.default_rng(6)
     B, T = 2, 4
@@ -250,8 +250,8 @@ def test_io_layouts_are_the_printed_planes():
     assert np.array_equal(synth.fs_t_c_to_sc_f_t(canon, S), planes)
 
 
-def test_c0_forward_runs_in_seconds_and_is_finite():
-    w = synth.WORKLOADS["c0_tiny_fp32"]
+def test_tiny_forward_runs_in_seconds_and_is_finite():
+    w = synth.WORKLOADS["tiny_fp32"]
     cfg = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads, w.dim_head)
     ws = synth.draw_weights(M.inventory(cfg), w.dtype, seed=w.weight_seed)
     x = synth.draw_input(w)

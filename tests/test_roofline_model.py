@@ -11,7 +11,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def test_flop_terms_match_printed_accounting():
     g = json.load(open(os.path.join(GOLDEN, "flop_terms.json")))
-    w = synth.WORKLOADS["c2_8s_bf16"]                   # the vocals model at 801 frames
+    w = synth.WORKLOADS["chunk8s_bf16"]                   # the vocals model at 801 frames
     s = roofline.shape_of(w, total_width=7916)
     f = roofline.flops_per_launch(s)
     L = w.depth
