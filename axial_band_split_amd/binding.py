@@ -39,7 +39,7 @@ _SIGS = {
     "mbr_k_gelu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]),
 }
 KERNEL_KINDS = ("gather", "embed", "norm", "qkv", "attn_time", "attn_band", "out_proj", "ffn1", "ffn2",
-                "mask_hidden", "mask_glu", "average")
+                "mask_hidden", "mask_glu", "average", "block")
 SYMBOLS = tuple(_SIGS)
 
 

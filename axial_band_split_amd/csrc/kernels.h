@@ -159,4 +159,23 @@ struct AverageLaunch {
 };
 hipError_t launch_average(const AverageLaunch& L, hipStream_t stream);
 
+// Out-projection, residual, feed-forward and both norms of one Transformer in one kernel
+// (16-bit operands).  stream: the weights as fragment-ordered stages (block_stream_elems(D, I, FF)
+// elements of the dtype, laid out by the creator).
+struct BlockLaunch {
+  int dtype;
+  const void* O;            // [tokens][I] gated attention output
+  const void* stream;
+  const float* b1;          // [FF]
+  const float* b2;          // [D]
+  const float* gout;        // [D] gamma_out * sqrt(D)
+  float* X;                 // [tokens][D] residual: x in, RMSNorm_out(x2) out
+  void* XH;                 // [tokens][D] 16-bit copy for the next product
+  int32_t tokens, D, I;
+  int32_t xh_norm;          // 1: XH = x3 / |x3| * sqrt(D); 0: XH = x3
+};
+bool block_supported(int dtype, int D, int I, int FF);
+int64_t block_stream_elems(int D, int I, int FF);
+hipError_t launch_block(const BlockLaunch& L, hipStream_t stream);
+
 }  // namespace mbr

@@ -100,6 +100,7 @@ struct FPacker {  // fp32 side tables (biases, gains, gate weights)
 
 struct TransformerW {
   size_t wqkv, wout, w1, w2;          // element offsets in the dtype weight block
+  size_t bstream = 0;                 // fused post-attention kernel: fragment-ordered weight stages
   size_t wg, bg, b1, b2, gout;        // float offsets
 };
 struct MaskW {
@@ -119,6 +120,7 @@ struct mbr_core {
   // 16-bit GEMM tile configuration per launch kind (k_gemm2.hip variants)
   int v_embed = 0, v_qkv = 0, v_out = 0, v_ffn1 = 0, v_ffn2 = 0, v_mask = 0, v_glu = 0;
   int glu_blk = 16;                   // value / gate pairing block of the last mask layer
+  bool use_block = false;             // 16-bit path with the fused post-attention kernel
   int kpad_total = 0, kpad_max = 0;
   // device memory
   char* wdev = nullptr;               // dtype weights
@@ -286,6 +288,49 @@ int setup_tables_and_groups(mbr_core* c) {
   return MBR_OK;
 }
 
+// Weights of the fused post-attention kernel (k_block.hip) as the stages it copies into LDS, each
+// stage D/8 fragments of 64 lanes x 8 elements in the order the lanes read them.  A fragment is
+// the A operand of one 32 x 32 x 16 product: lane l supplies row l % 32 and K elements
+// 8(l/32) .. 8(l/32)+7.
+//   stages 0 .. I/64-1: out-projection, K step ks of 4, tile t of D/32 (rows 32t..): W_out[row][k]
+//   stage I/64 + c:     W_1 rows of hidden chunk c (K steps s of D/16) with the columns permuted to
+//                       the accumulator's row order, then W_2 columns of chunk c-2 (tile t, step s2)
+//                       permuted to the order the hidden tile holds its rows.
+// The accumulator of a 32 x 32 product holds in lane l rows 8(v/4) + 4(l/32) + v%4 (v = 0..15); read
+// as a B operand, K step s of a 32-row tile takes v = 8(s%2) + e, i.e. row
+// perm(s, h, e) = 32(s/2) + 8(2(s%2) + e/4) + 4h + e%4 for lane half h and element e.
+std::vector<double> block_stream(int D, int I, int FF, const std::vector<double>& wout,
+                                 const std::vector<double>& w1g, const std::vector<double>& w2) {
+  const int DT = D / 32, KO = I / 64, NCH = FF / 32;
+  const size_t stage = (size_t)D * 64;
+  std::vector<double> out((size_t)(KO + NCH + 2) * stage, 0.0);
+  auto perm = [](int s, int h, int e) { return 32 * (s / 2) + 8 * (2 * (s % 2) + e / 4) + 4 * h + e % 4; };
+  for (int st = 0; st < KO; ++st)
+    for (int ks = 0; ks < 4; ++ks)
+      for (int t = 0; t < DT; ++t)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) {
+            const int row = 32 * t + l % 32, k = 64 * st + 16 * ks + 8 * (l / 32) + e;
+            out[st * stage + ((size_t)(ks * DT + t) * 64 + l) * 8 + e] = wout[(size_t)row * I + k];
+          }
+  for (int c = 0; c <= NCH + 1; ++c) {
+    const size_t base = (size_t)(KO + c) * stage;
+    if (c < NCH)
+      for (int s = 0; s < D / 16; ++s)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e)
+            out[base + ((size_t)s * 64 + l) * 8 + e] = w1g[(size_t)(32 * c + l % 32) * D + perm(s, l / 32, e)];
+    if (c > 1)
+      for (int t = 0; t < DT; ++t)
+        for (int s2 = 0; s2 < 2; ++s2)
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 8; ++e)
+              out[base + (size_t)(D / 16) * 512 + ((size_t)(2 * t + s2) * 64 + l) * 8 + e] =
+                  w2[(size_t)(32 * t + l % 32) * FF + 32 * (c - 2) + perm(s2, l / 32, e)];
+  }
+  return out;
+}
+
 int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
   const mbr_config& cfg = c->cfg;
   const Bands& bd = c->bands;
@@ -343,6 +388,7 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
     std::vector<double> gout(D);
     for (int e = 0; e < D; ++e) gout[e] = go[e] * std::sqrt((double)D);
     TransformerW& tw = c->tw[t];
+    if (c->use_block) tw.bstream = pk.append(block_stream(D, I, FF, wout, f1, w2));
     tw.wqkv = pk.append(q);
     tw.wout = pk.append(wout);
     tw.w1 = pk.append(f1);
@@ -527,9 +573,11 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     gq.dense.N = 3 * c->I + (fused ? 64 : 0);
     gq.dense.K = c->D;
     if (fused) {
-      gq.rowss = c->ssB;
-      gq.ss_parts = parts;
-      gq.rs_mul = sqrtD;
+      if (t == 0 || !c->use_block) {   // otherwise XH arrives normalised
+        gq.rowss = c->ssB;
+        gq.ss_parts = parts;
+        gq.rs_mul = sqrtD;
+      }
       gq.gates = c->gates;
       gq.gate_bias = c->fdev + tw.bg;
     }
@@ -567,6 +615,26 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     al.scale_log2 = 1.4426950408889634f;  // the 1/sqrt(dh) scale is folded into W_q
     LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME,
            (axis == 0 && dt != MBR_F32) ? launch_attention_time2(al, s) : launch_attention(al, s));
+
+    const bool last = t == ntr - 1;
+    if (c->use_block) {
+      BlockLaunch bl{};
+      bl.dtype = dt;
+      bl.O = c->O;
+      bl.stream = wptr(tw.bstream);
+      bl.b1 = c->fdev + tw.b1;
+      bl.b2 = c->fdev + tw.b2;
+      bl.gout = c->fdev + tw.gout;
+      bl.X = c->X;
+      bl.XH = c->XH;
+      bl.tokens = NT;
+      bl.D = c->D;
+      bl.I = c->I;
+      bl.xh_norm = last ? 0 : 1;
+      LAUNCH(MBR_K_BLOCK, launch_block(bl, s));
+      if (stop_stage == 1 + t) return MBR_OK;   // X holds x after the output norm
+      continue;
+    }
 
     GemmLaunch go{};
     go.dtype = dt;
@@ -644,7 +712,6 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     }
     LAUNCH(MBR_K_FFN2, gemm(g2, c->v_ffn2, s));
 
-    const bool last = t == ntr - 1;
     if (!fused) {
       NormLaunch no{dt, last ? 2 : 1, c->X, c->XH, c->fdev + tw.gout, last ? nullptr : c->gates,
                     last ? nullptr : c->fdev + c->tw[t + 1].wg, last ? nullptr : c->fdev + c->tw[t + 1].bg,
@@ -679,7 +746,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
         gm.C = dst;
         gm.ldc = c->MH;
         src = dst;
-        if (fused && j == 0) {   // the last Transformer's output norm, as a row scale
+        if (fused && !c->use_block && j == 0) {   // the last Transformer's output norm, as a row scale
           gm.rowss = c->ssA;
           gm.ss_parts = parts;
           gm.rs_mul = sqrtD;
@@ -803,8 +870,8 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->total = c->bands.total_width();
   const int kstep = cfg->dtype == MBR_F32 ? 16 : 32;
   c->glu_blk = cfg->dtype == MBR_F32 ? 16 : 32;
-  // tile configurations of the 16-bit GEMM per launch kind, from a sweep on MI355X at the core's
-  // shapes: 256 x 128 tiles of 64 x 64 waves where N = D is small, 256 x 256 for the wide products
+  // tile configuration of the 16-bit GEMM per launch kind, from a sweep on MI355X at the core's
+  // shapes: 256 x 128 tiles of 64 x 64 waves, 3 stages, was the fastest for every product
   c->v_qkv = 4;
   c->v_ffn1 = 4;
   c->v_ffn2 = 4;
@@ -812,6 +879,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->v_mask = 4;
   c->v_glu = 4;
   c->v_embed = 4;
+  c->use_block = block_supported(cfg->dtype, c->D, c->I, c->FF);
   c->kpad.resize(c->NB);
   c->kcol.resize(c->NB);
   c->wp.resize(c->NB);

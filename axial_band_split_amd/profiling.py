@@ -47,6 +47,9 @@ def short_name(k: str) -> str:
         if cfg:
             bm, wm, wn, ns = map(int, cfg.groups())
             tparts.append(f"{bm}x{64 * wn}/{wm}x{wn}w/{ns}st")
+        blk = re.search(r"BlockCfgI\w+?Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", rest)
+        if blk and name.startswith("block"):
+            tparts.append(f"D{blk.group(1)}/I{blk.group(2)}/{blk.group(3)}st")
         dh = re.search(r"Li(\d+)EEEv", rest)
         if dh and name.startswith("attn"):
             tparts.append(f"dh{dh.group(1)}")

@@ -69,6 +69,8 @@ def flops_per_launch(s: Shape) -> Dict[str, float]:
         "mask_hidden_first": 2.0 * BT * s.NB * D * s.MH,
         "mask_hidden_next": 2.0 * BT * s.NB * s.MH * s.MH,
         "mask_glu": 2.0 * BT * s.MH * 2 * s.total_width,
+        # out-projection + feed-forward of one Transformer in one kernel (16-bit path)
+        "block": 2.0 * N * I * D + 4.0 * N * D * s.FF,
     }
 
 

@@ -188,7 +188,9 @@ enum {
   MBR_K_MASK_HIDDEN = 9, /* mask MLP hidden layers (grouped GEMM, tanh)                  */
   MBR_K_MASK_GLU = 10,   /* mask MLP last layer + GLU (grouped GEMM)                     */
   MBR_K_AVERAGE = 11,    /* inverse-index mask average                                   */
-  MBR_K_COUNT = 12
+  MBR_K_BLOCK = 12,      /* 16-bit path: out-projection, residual, feed-forward and both
+                            norms of a Transformer in one kernel (replaces 6, 7, 8)      */
+  MBR_K_COUNT = 13
 };
 /*
  * The same forward as mbr_core_forward, with a HIP event pair recorded on `stream` around every

@@ -118,6 +118,32 @@ def test_fp32_stage_taps_match_oracle():
     assert rel_l2(y, ref) < 1e-5
 
 
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_half_precision_block_path_stage_taps(dtype):
+    """The 16-bit path of the vocals architecture (dim 384, 8 x 64 heads), where each Transformer's
+    out-projection, feed-forward and norms run as one kernel: x after every Transformer of a
+    two-layer core at 40 frames (2400 tokens, a ragged last group of 128) against the oracle's."""
+    w = synth.WORKLOADS["t256_fp16"].replace(frames=40, depth=2, dtype=dtype)
+    say(f"[taps] dim 384 {synth.DTYPE_NAMES[dtype]}, depth 2, T=40")
+    cfg, ws = build(w, std=0.05, gamma_std=0.3)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    xd = torch.from_numpy(x).cuda()
+    taps = M.Taps()
+    ref = M.forward(x, ocfg(w), ws, taps=taps)
+    B, T, NB, D = taps.embed.shape
+    for k, a in enumerate(taps.after):
+        got = core.debug(xd, 1 + k).cpu().numpy().reshape(NB, B, T, D)
+        e = rel_l2(got, a.transpose(2, 0, 1, 3))
+        say(f"[taps] transformer {k}: {e:.2e}")
+        assert e < TOL[dtype]
+    y = gpu_forward(core, x)
+    core.close()
+    err = rel_l2(y, ref)
+    say(f"[taps] masks: {err:.2e}")
+    assert err <= TOL[dtype]
+
+
 def test_batch_below_max_and_sc_f_t_layout():
     w = synth.WORKLOADS["tiny_fp32"].replace(batch=3, io_layout=synth.IO_SC_F_T)
     say("[parity] tiny layout 1, max_batch 3, batches 3, 2, 1")
