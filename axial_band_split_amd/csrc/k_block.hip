@@ -108,9 +108,10 @@ struct BlockCfg {
   static constexpr int SB = D * 128;
   static constexpr int R = SB / 4096;               // 16-byte loads per thread per stage
   static constexpr int LDS = NS * SB;               // the ring (b_1 is a static LDS array)
+  static_assert(DT % 3 == 0 && 9 * 16 * 64 * 4 <= NS * SB, "split-block reduction layout");
 };
 
-template <typename T, typename C>
+template <typename T, typename C, bool SPLIT_BLOCKS>
 __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   typedef typename Frag<T>::type frag;
   constexpr int D = C::D, I = C::I, NS = C::NS, DT = C::DT, NCH = C::NCH, KO = C::KO, NST = C::NST,
@@ -120,7 +121,12 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   __shared__ __attribute__((aligned(16))) float b1s[FF];        // b_1, a separate LDS object
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
-  const int64_t token = (int64_t)blockIdx.x * 128 + w * 32 + (lane & 31);
+  // Blocks below split_from own 128 tokens (a strip of 32 per wave).  The blocks after them take
+  // the tokens left over from whole rounds over the device one strip each: the four waves share
+  // the strip and split the hidden chunks (wave w runs chunks c = w mod 4), then add their parts.
+  constexpr bool split = SPLIT_BLOCKS;
+  const int64_t token = split ? (int64_t)L.split_from * 128 + (int64_t)blockIdx.x * 32 + (lane & 31)
+                              : (int64_t)blockIdx.x * 128 + w * 32 + (lane & 31);
   const bool valid = token < L.tokens;
   // lanes past the last token read the last token's row and store nothing (a token's lanes only
   // ever combine with each other)
@@ -198,6 +204,12 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   for (int s = 0; s < D / 16; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) xb[s][e] = cvt<T>(acc[s >> 1][8 * (s & 1) + e] * r1);
+  if (split && w != 0) {   // only wave 0 carries x1; the others accumulate their hidden chunks' part
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  }
 
   // ---- feed-forward onto x1, three chunks in flight: step c (stage KO + c, holding the W_1 rows
   // of chunk c and the W_2 columns of chunk c - 2) runs chunk c's first product, the GELU of chunk
@@ -207,8 +219,8 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   // at full rate on this matrix core, so the first product needs only one.)
   constexpr bool SPLIT = false;
   constexpr int N1 = D / 16, N2 = 2 * DT;
-  f32x16 hA0, hA1, hB0, hB1;
-  frag gA0, gA1, gB0, gB1;
+  f32x16 hA0{}, hA1{}, hB0{}, hB1{};
+  frag gA0{}, gA1{}, gB0{}, gB1{};
   auto step = [&](auto do1_, auto dog_, auto do2_, const char* sl, int c, f32x16& n0, f32x16& n1,
                   const f32x16& o0, const f32x16& o1, frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
     constexpr bool do1 = decltype(do1_)::value, dog = decltype(dog_)::value, do2 = decltype(do2_)::value;
@@ -243,43 +255,89 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
       }
     };
     // GELU value v of the lane's 16 (hidden rows 8(v/4) + 4h + v%4 of chunk c-1) in region
-    // 1 + v G / 16
+    // 1 + v G / 16 (all in "region 1" when there are no products)
     auto hook = [&](auto g_) {
       constexpr int g = decltype(g_)::value;
       if constexpr (dog) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (1 + v * G / 16 == g) {
+          if (G == 0 || 1 + v * G / 16 == g) {
             const float y = SPLIT ? o0[v] + o1[v] : o0[v];
             (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu_erf(y));
           }
       }
     };
-    pipelined<NA + NB, GS, 8, frag>(rd, mm, hook);
+    if constexpr (NA + NB == 0) {
+      hook(std::integral_constant<int, 1>{});
+    } else {
+      pipelined<NA + NB, GS, 8, frag>(rd, mm, hook);
+    }
   };
   using Y = std::true_type;
   using Nn = std::false_type;
   auto slot = [&](int c) { return smem + ((KO + c) % NS) * SB + lane * 16; };
+  // step c with the register roles of its parity; in a split block, wave w does only the part of
+  // the step that belongs to its chunks (first product of c, GELU of c-1 or second product of
+  // c-2, whichever is w's; the block still meets at every stage)
+  auto run = [&](auto d1, auto dg, auto d2, int c, f32x16& n0, f32x16& n1, const f32x16& o0, const f32x16& o1,
+                 frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
+    constexpr bool D1 = decltype(d1)::value, DG = decltype(dg)::value, D2 = decltype(d2)::value;
+    const char* sl = slot(c);
+    if constexpr (!split) {
+      step(d1, dg, d2, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
+    } else {
+      const int sel = (c - w) & 3;
+      if (D1 && sel == 0) step(Y{}, Nn{}, Nn{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
+      else if (DG && sel == 1) step(Nn{}, Y{}, Nn{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
+      else if (D2 && sel == 2) step(Nn{}, Nn{}, Y{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
+    }
+  };
   // c = 0, 1
   stage_begin(KO);
-  step(Y{}, Nn{}, Nn{}, slot(0), 0, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
+  run(Y{}, Nn{}, Nn{}, 0, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
   stage_end(KO);
   stage_begin(KO + 1);
-  step(Y{}, Y{}, Nn{}, slot(1), 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
+  run(Y{}, Y{}, Nn{}, 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
   stage_end(KO + 1);
   for (int c = 2; c < NCH; c += 2) {
     stage_begin(KO + c);
-    step(Y{}, Y{}, Y{}, slot(c), c, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
+    run(Y{}, Y{}, Y{}, c, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
     stage_end(KO + c);
     stage_begin(KO + c + 1);
-    step(Y{}, Y{}, Y{}, slot(c + 1), c + 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
+    run(Y{}, Y{}, Y{}, c + 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
     stage_end(KO + c + 1);
   }
   stage_begin(KO + NCH);
-  step(Nn{}, Y{}, Y{}, slot(NCH), NCH, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
+  run(Nn{}, Y{}, Y{}, NCH, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
   stage_end(KO + NCH);
   stage_begin(KO + NCH + 1);
-  step(Nn{}, Nn{}, Y{}, slot(NCH + 1), NCH + 1, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
+  run(Nn{}, Nn{}, Y{}, NCH + 1, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
+
+  if constexpr (split) {
+    // wave 0 adds the other waves' parts, three tiles per wave at a time through the (now idle)
+    // ring: lane-consecutive floats, [wave-1][tile][v][lane]
+    float* red = (float*)smem;
+#pragma unroll
+    for (int p = 0; p < DT / 3; ++p) {
+      block_barrier();
+      if (w != 0) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[(((w - 1) * 3 + q) * 16 + v) * 64 + lane] = acc[3 * p + q][v];
+      }
+      __syncthreads();
+      if (w == 0) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[3 * p + q][v] += red[((u * 3 + q) * 16 + v) * 64 + lane];
+      }
+    }
+    if (w != 0) return;
+  }
 
   // ---- x2 = acc + b_2;  x3 = RMSNorm_out(x2) -> X;  XH = x3 normalised (or x3)
   {
@@ -331,12 +389,22 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
 
 template <typename T, typename C>
 hipError_t launch_t(const BlockLaunch& L, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-  if (e != hipSuccess) return e;
-  const int blocks = (L.tokens + 127) / 128;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((block_kernel<T, C>), dim3(blocks), dim3(256), C::LDS, stream, L);
-  return hipGetLastError();
+  if (L.split_from < 0 || (int64_t)L.split_from * 128 > L.tokens) return hipErrorInvalidValue;
+  // blocks of 128 tokens, then one 32-token strip per block for the rest
+  if (L.split_from > 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((block_kernel<T, C, false>), dim3(L.split_from), dim3(256), C::LDS, stream, L);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int strips = (int)((L.tokens - (int64_t)L.split_from * 128 + 31) / 32);
+  if (strips > 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, true>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3(strips), dim3(256), C::LDS, stream, L);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <typename T>

@@ -173,6 +173,8 @@ struct BlockLaunch {
   void* XH;                 // [tokens][D] 16-bit copy for the next product
   int32_t tokens, D, I;
   int32_t xh_norm;          // 1: XH = x3 / |x3| * sqrt(D); 0: XH = x3
+  int32_t split_from;       // blocks [0, split_from) take 128 tokens each; the tokens after
+                            // split_from * 128 go 32 to a block, split over its waves by hidden chunk
 };
 bool block_supported(int dtype, int D, int I, int FF);
 int64_t block_stream_elems(int D, int I, int FF);

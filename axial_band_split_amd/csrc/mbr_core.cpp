@@ -115,6 +115,7 @@ struct mbr_core {
   mbr_config cfg;
   Bands bands;
   int device = 0;
+  int ncu = 256;                      // compute units of the device
   int NB = 0, D = 0, H = 0, DH = 0, I = 0, FF = 0, MH = 0, T = 0, Tp = 0, Bmax = 0, total = 0;
   std::vector<int> kpad, kcol, wp;    // per band: padded K of the embedding, U column block, mask N/2
   // 16-bit GEMM tile configuration per launch kind (k_gemm2.hip variants)
@@ -160,12 +161,13 @@ struct mbr_core {
 
 namespace {
 
-int check_device(int* dev) {
+int check_device(int* dev, int* ncu) {
   HIP_TRY(hipGetDevice(dev));
   hipDeviceProp_t p;
   HIP_TRY(hipGetDeviceProperties(&p, *dev));
   if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0)
     return fail(MBR_E_DEVICE, std::string("device is ") + p.gcnArchName + ", this library is built for gfx950");
+  *ncu = p.multiProcessorCount;
   return MBR_OK;
 }
 
@@ -618,6 +620,10 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
 
     const bool last = t == ntr - 1;
     if (c->use_block) {
+      // The fused kernel holds one group of 128 tokens per compute unit at a time: whole rounds
+      // over the device go 128 tokens to a block, the rest 32 to a block (a partial round of
+      // 128-token blocks would cost as much as a full one)
+      const int64_t round = (int64_t)128 * c->ncu;
       BlockLaunch bl{};
       bl.dtype = dt;
       bl.O = c->O;
@@ -631,6 +637,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
       bl.D = c->D;
       bl.I = c->I;
       bl.xh_norm = last ? 0 : 1;
+      bl.split_from = (int32_t)((int64_t)NT / round * round / 128);
       LAUNCH(MBR_K_BLOCK, launch_block(bl, s));
       if (stop_stage == 1 + t) return MBR_OK;   // X holds x after the output norm
       continue;
@@ -847,7 +854,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
     delete c;
     return fail(MBR_E_CONFIG, "invalid config: the band-axis attention supports at most 64 bands");
   }
-  rc = check_device(&c->device);
+  rc = check_device(&c->device, &c->ncu);
   if (rc) {
     delete c;
     return rc;
