@@ -2,20 +2,24 @@
 //
 // One sequence is one (batch, band) pair of the time Transformer, its positions the frames
 // ([P1] "The two transformers are not the same shape"); per head, o = softmax(q k^T) v with the
-// 1/sqrt(dh) scale already folded into W_q, times the head's gate ([P1] "Per Attention layer").
+// 1/sqrt(dh) scale already folded into W_q and q scaled by log2(e) by the projection's epilogue
+// (scores in log2 units), times the head's gate ([P1] "Per Attention layer").
 //
 //   * workgroup = 4 waves x 32 queries; the K tile [64 keys][dh] and the V^T tile [dh][64 keys]
 //     (V^T is written that way by the q/k/v projection) arrive by 16-byte direct global->LDS loads
 //     into a 2-stage ring, the next tile in flight while the current one is consumed;
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16: a lane owns one query column and 16 of
-//     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart, and its
-//     sum none until the end;
+//     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart; the S^T
+//     accumulators start at minus the running reference, so a probability is one exponential, and
+//     the row sums come from the matrix core (a ones row times P^T), leaving the vector units the
+//     exponentials, the tile max and the conversions;
 //   * the probabilities feed the P.V product straight from the S^T accumulators: the K rows of the
 //     S^T product are taken in a permuted order so that the 8 probabilities a lane holds for one
 //     16-key step belong to 8 consecutive keys, and the matching V^T operand is one 16-byte read;
-//   * the running max used for the exponentials is raised only when a tile's max exceeds it by more
-//     than 8 (log2 units); until then the accumulators need no rescaling.  Any reference value gives
-//     the same softmax, the bound keeps every exponential <= 2^8;
+//   * the reference used for the exponentials is the first tile's max, raised only when a later
+//     tile's max exceeds it by more than 8 (log2 units); until then the accumulators need no
+//     rescaling.  Any reference value gives the same softmax, the bound keeps every exponential
+//     <= 2^8;
 //   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by (row >> 1) & 7, so the rows one
 //     fragment read touches spread over all LDS banks;
 //   * only the last key tile is masked (keys >= n), and the workgroup order keeps all query blocks of
@@ -34,6 +38,14 @@ __device__ __forceinline__ void mma32(f32x16& c, const f16x8& a, const f16x8& b)
 }
 __device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// d = a b + c with c kept (a separate accumulator input)
+__device__ __forceinline__ f32x16 mma32c(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32c(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void dma16(const char* g, char* lds_wave_base) {
@@ -120,8 +132,20 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   for (int d = 0; d < DT; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[d][v] = 0.f;
-  float mref = kNegBig, lsum = 0.f;
-  const float c2 = L.scale_log2;
+  // row sums of P on the matrix core: an A operand whose row 0 is all ones turns each P^T step
+  // into column sums, which land in row 0 of lsacc (lanes 0..31, element 0)
+  f32x16 lsacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lsacc[v] = 0.f;
+  frag ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = cvt<T>(l32 == 0 ? 1.0f : 0.0f);
+  // q arrives scaled by log2(e) (and 1/sqrt(dh)), so scores are already in log2 units; the S^T
+  // accumulators start at -mref, so the products deliver s - mref and p = exp2 of it directly
+  float mref = 0.f;
+  f32x16 negm;   // -mref in every element: the C operand of each tile's first S^T step
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negm[v] = 0.f;
 
   const int ntiles = (n + KT - 1) / KT;
   issue(0);
@@ -134,14 +158,13 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     f32x16 s[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[r][v] = 0.f;
       const int row = r * 32 + perm(l32);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int lc = 2 * ks + g;
         const frag a = *(const frag*)(st + row * KROWB + ((lc ^ (swz8(row) % KCH)) << 4));
-        mma32(s[r], a, qf[ks]);
+        if (ks == 0) s[r] = mma32c(a, qf[0], negm);
+        else mma32(s[r], a, qf[ks]);
       }
     }
     if (kt == ntiles - 1 && (n & (KT - 1))) {
@@ -158,31 +181,29 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[r][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    if (__any(mx > mref + kLazy)) {
-      const float mnew = fmaxf(mref, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-      mref = mnew;
-      lsum *= alpha;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // the first tile sets the reference exactly; later ones move it only past kLazy
+    if (kt == 0 || __any(mx > kLazy)) {
+      const float up = kt == 0 ? mx : fmaxf(mx, 0.f);
+      if (kt > 0) {
+        const float alpha = __builtin_amdgcn_exp2f(-up);
 #pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] *= alpha;
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[r][v] * c2 - mref);
-        s[r][v] = p;
-        part += p;
+        for (int d = 0; d < DT; ++d) o[d] *= alpha;
+        lsacc *= alpha;
       }
-    lsum += part;
+      mref += up;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[v] = -mref;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) s[r] -= up;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int r = t >> 1, hv = (t & 1) * 8;
       frag pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(s[r][hv + e]);
+      for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(__builtin_amdgcn_exp2f(s[r][hv + e]));
+      mma32(lsacc, ones, pf);
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         // V^T row (head dim) d*32 + l32, keys 16t + 8g .. +7: one 16-byte chunk
@@ -193,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     }
   }
 
-  lsum += __shfl_xor(lsum, 32, 64);
+  const float lsum = __shfl(lsacc[0], l32, 64);
   const int q = q0 + l32;
   if (q >= n) return;
   const size_t row = (size_t)seq * L.frames + q;
@@ -222,7 +243,8 @@ hipError_t launch_t(const AttnLaunch& L, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream) {
-  if (L.npad % 128 || L.axis != 0) return hipErrorInvalidValue;
+  // q must carry log2(e): scores arrive in log2 units
+  if (L.npad % 128 || L.axis != 0 || L.scale_log2 != 1.0f) return hipErrorInvalidValue;
   switch (L.dtype) {
     case DT_F16: return launch_t<f16>(L, stream);
     case DT_BF16: return launch_t<bf16>(L, stream);

@@ -380,6 +380,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
               v[2 * q] = x0 * cc[q] - x1 * ss[q];
               v[2 * q + 1] = x0 * ss[q] + x1 * cc[q];
             }
+            if (which == 0) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] *= qa.q_mul;
+            }
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) p[e] = cvt<T>(v[e]);

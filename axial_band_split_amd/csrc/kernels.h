@@ -47,6 +47,7 @@ struct QkvArgs {
   const float* sin;
   int32_t axis;       // 0: time (seq = row / T, pos = row % T); 1: band (seq = row % (B*T), pos = row / (B*T))
   int32_t frames, batch, heads, dh, npad;
+  float q_mul;        // factor on q after the rotary step (16-bit path: log2(e), scores in log2 units)
 };
 
 struct GemmLaunch {

@@ -597,6 +597,8 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     qa.heads = c->H;
     qa.dh = c->DH;
     qa.npad = axis ? 64 : c->Tp;
+    // 16-bit path: q leaves the projection in log2 units for the exponentials of the attention
+    qa.q_mul = fused ? 1.4426950408889634f : 1.0f;
     LAUNCH(MBR_K_QKV, gemm(gq, c->v_qkv, s));
 
     AttnLaunch al{};
@@ -614,7 +616,8 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     al.dh = c->DH;
     al.frames = c->T;
     al.batch = batch;
-    al.scale_log2 = 1.4426950408889634f;  // the 1/sqrt(dh) scale is folded into W_q
+    // the 1/sqrt(dh) scale is folded into W_q; the 16-bit projection also applies log2(e)
+    al.scale_log2 = fused ? 1.0f : 1.4426950408889634f;
     LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME,
            (axis == 0 && dt != MBR_F32) ? launch_attention_time2(al, s) : launch_attention(al, s));
 
