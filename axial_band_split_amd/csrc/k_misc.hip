@@ -165,15 +165,35 @@ hipError_t norm_t(const NormLaunch& L, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------- band gather
-// [P1] "The forward chain" and "The mel-band split, exactly": each band takes its (bin, channel)
-// pairs in order, real and imaginary part as neighbouring features, and is normalised over its own
-// features (the gain and sqrt(W_i) are folded into the band's projection).  Workgroup per
-// (64 frames, batch, band); lanes run along frames so every input load is coalesced; the band's
-// rows are assembled in LDS and written out as one contiguous block of U.
-template <typename T>
+// One (re, im) pair of the output in one LDS / global unit: 4 bytes for 16-bit types, 8 for fp32.
+template <typename T> struct PairUnit;
+template <> struct PairUnit<float> { typedef float2 type; static __device__ type make(float a, float b) { return make_float2(a, b); } };
+template <> struct PairUnit<f16> {
+  typedef uint32_t type;
+  static __device__ type make(float a, float b) {
+    const f16 x = cvt<f16>(a), y = cvt<f16>(b);
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+};
+template <> struct PairUnit<bf16> {
+  typedef uint32_t type;
+  static __device__ type make(float a, float b) {
+    const bf16 x = cvt<bf16>(a), y = cvt<bf16>(b);
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+};
+
+// Band gather with the band's RMSNorm ([P1] "The forward chain", BandSplit): for 64 frames of one
+// band, each lane (one frame) reads the band's (re, im) pairs along its frames (coalesced along
+// the time axis of the input), the row norm comes from a first pass, and the normalised pairs are
+// transposed through LDS (rows of kpad/2 + 1 units, so the 64 lanes of a column write fall on
+// distinct banks) into the band's block of U, whose rows (frames) are contiguous.
+template <typename T, int LAYOUT>
 __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch L) {
+  typedef typename PairUnit<T>::type P;
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  T* tile = (T*)lds_raw;                       // [64][kpad]
+  P* tile = (P*)lds_raw;                       // [64][kpad/2 + 1]
+  int* pidx = (int*)(tile + 64 * (L.max_kpad / 2 + 1));   // the band's pair indices
   __shared__ float part[4][64];
   __shared__ float scale[64];
   const int band = blockIdx.z, b = blockIdx.y;
@@ -183,25 +203,28 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch L) {
   const bool valid = t < L.frames;
   const int foff = L.band_info[band * 4 + 0], width = L.band_info[band * 4 + 1];
   const int kpad = L.band_info[band * 4 + 2], ucol = L.band_info[band * 4 + 3];
-  const int npairs = width / 2;
-  const int* pairs = L.gather_pair + foff / 2;
+  const int npairs = width / 2, kp2 = kpad / 2, rs = kp2 + 1;
   const int F = L.n_freqs, S = L.channels, FS = F * S, T_ = L.frames;
+  for (int j = threadIdx.x; j < npairs; j += 256) pidx[j] = L.gather_pair[foff / 2 + j];
+  __syncthreads();
+  // lanes past the last frame read frame T-1 and are never stored
+  const int tl = valid ? t : T_ - 1;
   auto load = [&](int p, float& re, float& im) {
-    if (!valid) { re = im = 0.f; return; }
-    if (L.layout == 0) {
-      const float2 z = *(const float2*)(L.in + (((size_t)b * FS + p) * T_ + t) * 2);
+    if constexpr (LAYOUT == 0) {
+      const float2 z = *(const float2*)(L.in + (((size_t)b * FS + p) * T_ + tl) * 2);
       re = z.x; im = z.y;
     } else {
       const int f = p / S, s = p - f * S;
-      const float* base = L.in + ((size_t)b * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + t;
+      const float* base = L.in + ((size_t)b * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + tl;
       re = base[0];
       im = base[(size_t)F * T_];
     }
   };
   float ss = 0.f;
+#pragma unroll 16
   for (int j = wq; j < npairs; j += 4) {
     float re, im;
-    load(pairs[j], re, im);
+    load(pidx[j], re, im);
     ss += re * re + im * im;
   }
   part[wq][lane] = ss;
@@ -212,20 +235,30 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch L) {
   }
   __syncthreads();
   const float sc = scale[lane];
-  for (int j = wq; j < npairs; j += 4) {
-    float re, im;
-    load(pairs[j], re, im);
-    tile[lane * kpad + 2 * j] = cvt<T>(re * sc);
-    tile[lane * kpad + 2 * j + 1] = cvt<T>(im * sc);
+  // sixteen pairs per batch: all index reads, then all loads, then all LDS stores (the stores would
+  // otherwise keep the next index read, and so the next load, waiting)
+  for (int j0 = wq; j0 < npairs; j0 += 64) {
+    float re[16], im[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + 4 * u;
+      const int pj = pidx[j < npairs ? j : j0];
+      load(pj, re[u], im[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + 4 * u;
+      if (j < npairs) tile[lane * rs + j] = PairUnit<T>::make(re[u] * sc, im[u] * sc);
+    }
   }
-  for (int e = width + wq; e < kpad; e += 4) tile[lane * kpad + e] = cvt<T>(0.f);
+  for (int j = npairs + wq; j < kp2; j += 4) tile[lane * rs + j] = PairUnit<T>::make(0.f, 0.f);
   __syncthreads();
-  // rows b*T + t0 .. of band `band`: contiguous in U at column block ucol
+  // rows b*T + t0 .. of band `band`: contiguous in U at column block ucol, kpad/2 units a row
   const int rows = min(64, T_ - t0);
   const size_t BT = (size_t)L.batch * T_;
-  T* dst = (T*)L.U + (size_t)ucol * BT + ((size_t)b * T_ + t0) * kpad;
-  const int n16 = rows * kpad * (int)sizeof(T) / 16;
-  for (int c = threadIdx.x; c < n16; c += 256) ((uint4*)dst)[c] = ((const uint4*)tile)[c];
+  P* dst = (P*)((T*)L.U + (size_t)ucol * BT + ((size_t)b * T_ + t0) * kpad);
+  for (int r = wq; r < rows; r += 4)
+    for (int c = lane; c < kp2; c += 64) dst[(size_t)r * kp2 + c] = tile[r * rs + c];
 }
 
 // ---------------------------------------------------------------------------------- average
@@ -287,11 +320,13 @@ hipError_t launch_norm(const NormLaunch& L, hipStream_t stream) {
 template <typename T>
 hipError_t gather_t(const GatherLaunch& L, hipStream_t stream) {
   dim3 grid((L.frames + 63) / 64, L.batch, L.num_bands), block(256);
-  const size_t lds = (size_t)64 * L.max_kpad * sizeof(T);
+  const size_t lds = (size_t)64 * (L.max_kpad / 2 + 1) * 2 * sizeof(T) + (size_t)(L.max_kpad / 2) * 4;
   if (lds > 160 * 1024 - 2048) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)gather_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* k = L.layout == 0 ? (const void*)gather_kernel<T, 0> : (const void*)gather_kernel<T, 1>;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gather_kernel<T>, grid, block, lds, stream, L);
+  if (L.layout == 0) hipLaunchKernelGGL((gather_kernel<T, 0>), grid, block, lds, stream, L);
+  else hipLaunchKernelGGL((gather_kernel<T, 1>), grid, block, lds, stream, L);
   return hipGetLastError();
 }
 
