@@ -10,9 +10,10 @@
 //     loads with s_waitcnt and the workgroup meets at one barrier per step;
 //   * rows are stored with their four 16-byte chunks XOR-permuted by ((row>>1) ^ (row>>2)) & 3 so
 //     the 32 rows one fragment read touches fall on distinct LDS banks;
-//   * dense launches walk the tiles so that each XCD (workgroups are dealt round-robin to the 8
-//     XCDs) receives one contiguous run of tiles: neighbouring tiles share their A panel in that
-//     XCD's L2;
+//   * launches walk the tiles (dense order, or the grouped launch's tile table, where a group's
+//     tiles are consecutive) so that each XCD (workgroups are dealt round-robin to the 8 XCDs)
+//     receives one contiguous run of tiles: neighbouring tiles share operand panels in that XCD's
+//     L2;
 //   * the epilogue stages 32 accumulator rows of a wave at a time through LDS and writes 16-byte
 //     vectors: rows of q, k, v (rotary applied to the pairs a lane already holds; the time axis'
 //     v transposed), GELU / tanh outputs, fp32 residual updates, and the GLU of paired 32-feature
@@ -83,16 +84,18 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
   const int M = L.M;
   GemmGroup g;
   int m0, n0;
+  // workgroups are dealt round-robin to the 8 XCDs: walk the tiles so that each XCD gets one
+  // contiguous run of them (neighbouring tiles share operand panels in that XCD's L2)
+  const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int logical = xcd * per + min(xcd, rem) + slot;
   if (L.tiles) {
-    const GemmTile t = L.tiles[blockIdx.x];
+    const GemmTile t = L.tiles[logical];
     g = L.groups[t.group];
     m0 = t.m0;
     n0 = t.n0;
   } else {
     g = L.dense;
-    const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int logical = x * per + min(x, rem) + slot;
     const int tn = (g.N + BN - 1) / BN;
     m0 = (logical / tn) * BM;
     n0 = (logical % tn) * BN;

@@ -5,6 +5,8 @@
     python -m axial_band_split_amd.profiling traffic  <fetch.csv> <write.csv> <cal_fetch.csv> <cal_write.csv>
                                                       <kernel regex> <out.json> --command "<cmd>"
     python axial_band_split_amd/profiling.py calibrate   (run under rocprofv3 --pmc: one device copy)
+    python -m axial_band_split_amd.profiling roofline <kernel_stats.csv> <fetch.csv> <write.csv> <cal_fetch.csv>
+                                                      <cal_write.csv> <sq.csv> <workload> <out.md> --command "<cmd>"
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into bytes per launch,
 each scaled by what the same counter reads for a plain device copy of known size (the calibration
@@ -107,11 +109,16 @@ def source_hash() -> str:
 
 
 def _one(csv_path: str, counter: str, regex: str) -> float:
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
-            if r["Counter_Name"] == counter and re.search(regex, r["Kernel_Name"])]
-    if not vals:
+    """Mean of a counter per dispatch for each kernel the pattern matches, summed over those kernels
+    (a kernel class launched as several kernels, e.g. the fused block's two instantiations, counts
+    as one launch of all of them)."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and re.search(regex, r["Kernel_Name"]):
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    if not per:
         raise SystemExit(f"no {counter} rows for /{regex}/ in {csv_path}")
-    return sum(vals) / len(vals)
+    return sum(sum(v) / len(v) for v in per.values())
 
 
 def traffic_record(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, regex, command) -> dict:
@@ -128,6 +135,62 @@ def traffic_record(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, regex, co
             "bytes_per_launch": fetch_kib * 1024 * ff + write_kib * 1024 * wf,
             "calibration": f"device copy of {CAL_BYTES} bytes: FETCH_SIZE {cal_fetch:.0f} KiB, WRITE_SIZE {cal_write:.0f} KiB",
             "source_sha": source_hash(), "command": command}
+
+
+N_SIMD, N_XCD = 1024, 8      # MI355X: 256 compute units x 4 SIMDs, 8 XCDs
+
+
+def roofline_md(stats_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, sq_csv, workload, command) -> str:
+    """Per kernel class of one forward: rocprofv3 average duration, algorithmic work against the
+    MI355X peak, calibrated HBM bytes and the matrix-core busy fraction from the SQ counters."""
+    import re as _re
+    sys.path.insert(0, os.path.dirname(HERE))
+    from axial_band_split_amd import roofline as R, synth, binding
+    w = synth.WORKLOADS[workload]
+    _, total_width, _ = binding.mbr_core_table_sizes(binding.config(w))
+    shp = R.shape_of(w, total_width)
+    flops = R.flops_per_launch(shp)
+    flops["mask_hidden"] = (flops["mask_hidden_first"] + (w.mask_depth - 1) * flops["mask_hidden_next"]) / w.mask_depth
+    byts = R.bytes_per_launch(shp)
+    byts["norm"] = byts["norm_out"]
+    stats = list(csv.DictReader(open(stats_csv)))
+    cal_f = max(float(r["Counter_Value"]) for r in csv.DictReader(open(cal_fetch_csv)) if r["Counter_Name"] == "FETCH_SIZE")
+    cal_w = max(float(r["Counter_Value"]) for r in csv.DictReader(open(cal_write_csv)) if r["Counter_Name"] == "WRITE_SIZE")
+    ff, wf = CAL_BYTES / (cal_f * 1024), CAL_BYTES / (cal_w * 1024)
+    rows = ["# Roofline of one forward, " + workload, "", f"Command: `{command}`", "",
+            f"Peaks: MFMA {R.PEAK_MFMA_TFLOPS[w.dtype]:.0f} TFLOP/s ({synth.DTYPE_NAMES[w.dtype]}), HBM "
+            f"{R.PEAK_HBM_GBS:.0f} GB/s.  HBM bytes = FETCH_SIZE x {ff:.3f} + WRITE_SIZE x {wf:.3f} (a {CAL_BYTES >> 20} MiB "
+            "device copy reads those factors).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x "
+            "GRBM_GUI_ACTIVE / 8 XCDs).  A kernel class launched as several kernels sums them per launch.", "",
+            "| kernel class | kernels | avg us / launch | work / launch | achieved | % of peak | HBM bytes / launch (measured) | measured GB/s | MFMA busy |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for kind, rx in R.KIND_REGEX.items():
+        names = [r["Name"] for r in stats if _re.search(rx, r["Name"])]
+        if not names:
+            continue
+        avg_us = sum(float(r["AverageNs"]) for r in stats if r["Name"] in names) / 1e3
+        try:
+            hbm = _one(fetch_csv, "FETCH_SIZE", rx) * 1024 * ff + _one(write_csv, "WRITE_SIZE", rx) * 1024 * wf
+        except SystemExit:
+            hbm = float("nan")
+        busy = float("nan")
+        try:
+            mb = _one(sq_csv, "SQ_VALU_MFMA_BUSY_CYCLES", rx)
+            ga = _one(sq_csv, "GRBM_GUI_ACTIVE", rx)
+            busy = mb / (N_SIMD * ga / N_XCD)
+        except SystemExit:
+            pass
+        if kind in R.MFMA_KINDS:
+            f = flops[kind]
+            ach = f / (avg_us * 1e-6) / 1e12
+            work, achs, frac = f"{f / 1e9:.1f} GFLOP", f"{ach:.0f} TFLOP/s", ach / R.PEAK_MFMA_TFLOPS[w.dtype]
+        else:
+            bb = byts.get(kind, float("nan"))
+            ach = bb / (avg_us * 1e-6) / 1e9
+            work, achs, frac = f"{bb / 1e6:.1f} MB", f"{ach:.0f} GB/s", ach / R.PEAK_HBM_GBS
+        rows.append(f"| {kind} | {len(names)} | {avg_us:.1f} | {work} | {achs} | {100 * frac:.1f}% | {hbm / 1e6:.1f} MB | "
+                    f"{hbm / (avg_us * 1e-6) / 1e9:.0f} | {100 * busy:.1f}% |")
+    return "\n".join(rows) + "\n"
 
 
 def calibrate() -> None:
@@ -152,9 +215,17 @@ def main(argv=None):
         c.add_argument(n)
     c.add_argument("--command", required=True)
     sub.add_parser("calibrate")
+    d = sub.add_parser("roofline")
+    for n in ("stats", "fetch", "write", "cal_fetch", "cal_write", "sq", "workload", "out"):
+        d.add_argument(n)
+    d.add_argument("--command", required=True)
     args = ap.parse_args(argv)
     if args.what == "calibrate":
         calibrate()
+        return 0
+    if args.what == "roofline":
+        open(args.out, "w").write(roofline_md(args.stats, args.fetch, args.write, args.cal_fetch, args.cal_write,
+                                              args.sq, args.workload, args.command))
         return 0
     if args.what == "stats":
         open(args.out, "w").write(stats_md(args.csv, args.command))

@@ -53,6 +53,17 @@ def shape_of(w: synth.Workload, total_width: int, batch: int | None = None) -> S
                  channels=w.audio_channels, esz=4 if w.dtype == synth.F32 else 2)
 
 
+# rocprofv3 kernel-name patterns of each kernel class on the 16-bit path (the GEMM's epilogue id is
+# its second template argument)
+KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E", "qkv": r"gemm2_kernelIDF16b?_?Li1E",
+              "ffn1": r"gemm2_kernelIDF16b?_?Li2E", "out_proj": r"gemm2_kernelIDF16b?_?Li3E",
+              "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
+              "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
+              "norm": r"norm", "gather": r"gather", "average": r"average", "block": r"block_kernel"}
+MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block")
+HBM_KINDS = ("gather", "average", "attn_band", "norm")
+
+
 def flops_per_launch(s: Shape) -> Dict[str, float]:
     """FLOPs of one launch of each kernel class (per Transformer for the trunk kernels)."""
     N, D, I, H = s.tokens, s.D, s.inner, s.H
@@ -96,4 +107,7 @@ def bytes_per_launch(s: Shape) -> Dict[str, float]:
         "norm_out": N * D * 4.0 * 2 + N * D * s.esz,             # read x, write x and x^
         "average": 4.0 * s.stems * BT * s.total_width + s.stems * spec,
         "attn_band": 4.0 * N * s.inner * s.esz,                   # q, k, v read, o written
+        # fused post-attention kernel: o read, x read and written (fp32), x^ written, weights once
+        "block": N * s.inner * s.esz + N * D * 8.0 + N * D * s.esz
+                 + (s.inner / 64 + s.FF / 32 + 2) * D * 64 * s.esz,
     }

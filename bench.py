@@ -26,13 +26,8 @@ import numpy as np  # noqa: E402
 from axial_band_split_amd import binding, roofline, synth  # noqa: E402
 
 METRIC = "core audio-seconds/sec (44.1 kHz stereo) at T=1100; attn+GEMM TFLOP/s vs peak"
-# rocprofv3 kernel-name patterns of each kernel class on the 16-bit path (epilogue template ids)
-KIND_REGEX = {"embed": r"gemm2_kernel.*Li0E", "qkv": r"gemm2_kernel.*Li1E", "ffn1": r"gemm2_kernel.*Li2E",
-              "out_proj": r"gemm2_kernel.*Li3E", "mask_hidden": r"gemm2_kernel.*Li4E",
-              "mask_glu": r"gemm2_kernel.*Li5E", "ffn2": r"gemm2_kernel.*Li7E", "attn_time": r"attn_time2",
-              "attn_band": r"attn_band", "norm": r"norm", "gather": r"gather", "average": r"average",
-              "block": r"block_kernel"}
-MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block")
+KIND_REGEX = roofline.KIND_REGEX
+MFMA_KINDS = roofline.MFMA_KINDS
 GEMM_ATTN_KINDS = MFMA_KINDS + ("attn_band",)
 
 
