@@ -389,7 +389,8 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
 
 template <typename T, typename C>
 hipError_t launch_t(const BlockLaunch& L, hipStream_t stream) {
-  if (L.split_from < 0 || (int64_t)L.split_from * 128 > L.tokens) return hipErrorInvalidValue;
+  // the last 128-token block may be partial only when no strips follow it
+  if (L.split_from < 0 || (int64_t)L.split_from * 128 >= (int64_t)L.tokens + 128) return hipErrorInvalidValue;
   // blocks of 128 tokens, then one 32-token strip per block for the rest
   if (L.split_from > 0) {
     hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
@@ -397,7 +398,8 @@ hipError_t launch_t(const BlockLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL((block_kernel<T, C, false>), dim3(L.split_from), dim3(256), C::LDS, stream, L);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int strips = (int)((L.tokens - (int64_t)L.split_from * 128 + 31) / 32);
+  const int64_t rest = (int64_t)L.tokens - (int64_t)L.split_from * 128;
+  const int strips = rest > 0 ? (int)((rest + 31) / 32) : 0;
   if (strips > 0) {
     hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, true>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;

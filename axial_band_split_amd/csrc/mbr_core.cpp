@@ -624,9 +624,12 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     const bool last = t == ntr - 1;
     if (c->use_block) {
       // The fused kernel holds one group of 128 tokens per compute unit at a time: whole rounds
-      // over the device go 128 tokens to a block, the rest 32 to a block (a partial round of
-      // 128-token blocks would cost as much as a full one)
+      // over the device go 128 tokens to a block.  The rest go 32 to a block (each such block
+      // streams all the weights for a quarter of the tokens, about half a round's time) when they
+      // fit on the device at once, else they take one more, partial round of 128-token blocks.
       const int64_t round = (int64_t)128 * c->ncu;
+      const int64_t rest_strips = ((int64_t)NT % round + 31) / 32;
+      const int64_t full = (int64_t)NT / round * round + (rest_strips > c->ncu ? (int64_t)NT % round : 0);
       BlockLaunch bl{};
       bl.dtype = dt;
       bl.O = c->O;
@@ -640,7 +643,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
       bl.D = c->D;
       bl.I = c->I;
       bl.xh_norm = last ? 0 : 1;
-      bl.split_from = (int32_t)((int64_t)NT / round * round / 128);
+      bl.split_from = (int32_t)((full + 127) / 128);
       LAUNCH(MBR_K_BLOCK, launch_block(bl, s));
       if (stop_stage == 1 + t) return MBR_OK;   // X holds x after the output norm
       continue;

@@ -5,6 +5,7 @@
     python -m axial_band_split_amd.profiling traffic  <fetch.csv> <write.csv> <cal_fetch.csv> <cal_write.csv>
                                                       <kernel regex> <out.json> --command "<cmd>"
     python axial_band_split_amd/profiling.py calibrate   (run under rocprofv3 --pmc: one device copy)
+    python -m axial_band_split_amd.profiling sweep <bench line .json> ... <out.md> --command "<cmd>"
     python -m axial_band_split_amd.profiling roofline <kernel_stats.csv> <fetch.csv> <write.csv> <cal_fetch.csv>
                                                       <cal_write.csv> <sq.csv> <workload> <out.md> --command "<cmd>"
 
@@ -193,6 +194,25 @@ def roofline_md(stats_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, s
     return "\n".join(rows) + "\n"
 
 
+def sweep_md(paths, command) -> str:
+    """One row per bench line: the workload's shape, throughput and the per-kernel device time."""
+    recs = [json.loads(open(p).read().strip().splitlines()[-1]) for p in paths]
+    kinds = []
+    for r in recs:
+        for k in r["kernels"]:
+            if k not in kinds:
+                kinds.append(k)
+    lines = ["# Throughput against the workload's shape", "", f"Commands: `{command}`", "",
+             "| workload | B | T | stems | ms / step | audio-s/s | attn+GEMM TFLOP/s | " + " | ".join(f"{k} ms" for k in kinds) + " |",
+             "|---|---|---|---|---|---|---|" + "---|" * len(kinds)]
+    for r in recs:
+        c = r["config"]
+        lines.append(f"| {c['workload']} | {c['batch']} | {c['frames']} | {c.get('stems', 1)} | {r['ms_per_step']:.3f} | "
+                     f"{r['value']:.1f} | {r['attn_gemm']['tflops']:.0f} | "
+                     + " | ".join(f"{r['kernels'][k]['ms_per_step']:.3f}" if k in r["kernels"] else "-" for k in kinds) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def calibrate() -> None:
     """One device-to-device copy of CAL_BYTES on the GPU: the known-size kernel whose FETCH_SIZE and
     WRITE_SIZE readings scale the counters of the library's kernels."""
@@ -215,6 +235,9 @@ def main(argv=None):
         c.add_argument(n)
     c.add_argument("--command", required=True)
     sub.add_parser("calibrate")
+    e = sub.add_parser("sweep")
+    e.add_argument("paths", nargs="+")
+    e.add_argument("--command", required=True)
     d = sub.add_parser("roofline")
     for n in ("stats", "fetch", "write", "cal_fetch", "cal_write", "sq", "workload", "out"):
         d.add_argument(n)
@@ -222,6 +245,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.what == "calibrate":
         calibrate()
+        return 0
+    if args.what == "sweep":
+        open(args.paths[-1], "w").write(sweep_md(args.paths[:-1], args.command))
         return 0
     if args.what == "roofline":
         open(args.out, "w").write(roofline_md(args.stats, args.fetch, args.write, args.cal_fetch, args.cal_write,

@@ -99,6 +99,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunk11s_fp16", choices=list(synth.WORKLOADS))
+    ap.add_argument("--frames", type=int, default=0, help="override the workload's frames per chunk")
+    ap.add_argument("--stems", type=int, default=0, help="override the number of mask heads")
+    ap.add_argument("--batch", type=int, default=0, help="override the chunks per call")
     ap.add_argument("--profile-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -112,6 +115,9 @@ def main() -> int:
         return 1
 
     w = synth.WORKLOADS[args.workload]
+    over = {k: v for k, v in (("frames", args.frames), ("num_stems", args.stems), ("batch", args.batch)) if v}
+    if over:
+        w = w.replace(**over, name=w.name + "".join(f"@{k}={v}" for k, v in over.items()))
     log(f"[bench] workload {w.name}: B={w.batch} T={w.frames} D={w.dim} depth={w.depth} "
         f"dtype={synth.DTYPE_NAMES[w.dtype]}")
     cfg = binding.config(w)
@@ -187,10 +193,11 @@ def main() -> int:
         log(f"[bench] cpu baseline: {cpu['value']:.4f} audio-s/s ({cpu['sample']})")
 
     line = {
-        "metric": METRIC, "value": value, "unit": "audio-s/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if w.frames == 1100 else METRIC.replace("T=1100", f"T={w.frames}"), "value": value, "unit": "audio-s/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": synth.DTYPE_NAMES[w.dtype], "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "frames": w.frames, "bands": w.num_bands, "dim": w.dim,
+        "config": {"workload": w.name, "batch": w.batch, "frames": w.frames, "stems": w.num_stems,
+                   "bands": w.num_bands, "dim": w.dim,
                    "depth": w.depth, "heads": w.heads, "dim_head": w.dim_head, "io_layout": w.io_layout,
                    "audio_seconds_per_step": w.audio_seconds},
         "roofline": roof,

@@ -203,3 +203,64 @@ def test_heavy_full_size_batch_consistency():
     assert torch.isfinite(y4).all()
     assert torch.equal(y4[2:3], y1)
     core.close()
+
+
+@pytest.mark.parametrize("name,dtype,frames,depth", [("tiny_fp32", synth.F32, 32, 1), ("t256_fp16", synth.F16, 48, 1)])
+def test_two_stem_heads_match_oracle(name, dtype, frames, depth):
+    """Two mask heads on one trunk ([P1] "Model family": the two-stem checkpoints): masks
+    [B, 2, ...], each stem's head checked against the oracle."""
+    w = synth.WORKLOADS[name].replace(num_stems=2, dtype=dtype, frames=frames, depth=depth)
+    say(f"[stems] {name} x2 stems, T={frames}, {synth.DTYPE_NAMES[dtype]}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, ocfg(w), ws)
+    assert y.shape == ref.shape and y.shape[1] == 2
+    for s in range(2):
+        err = rel_l2(y[:, s], ref[:, s])
+        say(f"[stems] stem {s}: rel L2 = {err:.3e}")
+        assert err <= TOL[dtype]
+
+
+def test_two_stems_full_size_with_a_copied_head_are_bitwise_one_stem():
+    """At 1100 frames, fp16: a two-stem core whose second head is a copy of the first gives that
+    head's masks twice, each bitwise equal to the one-stem core's (the heads share the trunk and
+    never interact)."""
+    w1 = synth.WORKLOADS["chunk11s_fp16"]
+    w2 = w1.replace(num_stems=2)
+    say("[stems] full size, copied head")
+    cfg1, ws1 = build(w1)
+    cfg2 = binding.config(w2)
+    inv2 = binding.inventory(cfg2)
+    head = len(inv2) - len(binding.inventory(cfg1))          # tensors of one stem's head
+    ws2 = list(ws1) + list(ws1[len(ws1) - head:])
+    assert [tuple(a.shape) for a in ws2] == [tuple(s) for _, s, _ in inv2]
+    xd = torch.from_numpy(synth.draw_input(w1)).cuda()
+    c1 = binding.Core(cfg1, ws1)
+    y1 = c1.forward(xd)
+    torch.cuda.synchronize()
+    c1.close()
+    c2 = binding.Core(cfg2, ws2)
+    y2 = c2.forward(xd)
+    torch.cuda.synchronize()
+    c2.close()
+    assert y2.shape[1] == 2
+    assert torch.equal(y2[:, 0], y1) and torch.equal(y2[:, 1], y1)
+
+
+@pytest.mark.parametrize("frames", [1, 97, 2200])
+def test_frame_counts_off_the_presets(frames):
+    """The vocals architecture (one layer) at 1 frame (every time sequence is one key), 97 frames
+    (ragged tiles everywhere) and 2200 frames (a 22 s chunk, twice the longest preset)."""
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(frames=frames, depth=1)
+    say(f"[frames] T={frames}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    err = rel_l2(y, M.forward(x, ocfg(w), ws))
+    say(f"[frames] T={frames}: rel L2 = {err:.3e}")
+    assert err <= TOL[w.dtype]
