@@ -46,7 +46,8 @@ SYMBOLS = tuple(_SIGS)
 class MbrConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "sample_rate", "n_fft", "audio_channels", "num_bands", "dim", "depth", "heads", "dim_head", "ff_mult",
-        "mask_hidden_mult", "mask_depth", "num_stems", "max_batch", "frames", "dtype", "io_layout")]
+        "mask_hidden_mult", "mask_depth", "num_stems", "max_batch", "frames", "dtype", "io_layout", "zero_dc")] + [
+        ("band_bins", C.POINTER(C.c_int32))]
 
 
 class MbrError(RuntimeError):
@@ -84,9 +85,15 @@ def config(w: synth.Workload, max_batch: int | None = None, **override) -> MbrCo
                 dim=w.dim, depth=w.depth, heads=w.heads, dim_head=w.dim_head, ff_mult=w.ff_mult,
                 mask_hidden_mult=w.mask_hidden_mult, mask_depth=w.mask_depth, num_stems=w.num_stems,
                 max_batch=w.batch if max_batch is None else max_batch, frames=w.frames, dtype=w.dtype,
-                io_layout=w.io_layout)
+                io_layout=w.io_layout, zero_dc=w.zero_dc, band_bins=w.band_bins)
     vals.update(override)
-    return MbrConfig(**vals)
+    bins = vals.pop("band_bins")
+    cfg = MbrConfig(**vals)
+    if bins is not None:
+        arr = (C.c_int32 * len(bins))(*bins)
+        cfg._bins = arr                      # kept alive with the structure
+        cfg.band_bins = C.cast(arr, C.POINTER(C.c_int32))
+    return cfg
 
 
 # ----------------------------------------------------------------------------- C entry points

@@ -850,6 +850,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   mbr_core* c = new (std::nothrow) mbr_core();
   if (!c) return fail(MBR_E_NOMEM, "host allocation failed");
   c->cfg = *cfg;
+  c->cfg.band_bins = nullptr;   // the caller's table is read here only; the bands keep it
   std::string err;
   int rc = build_bands(*cfg, &c->bands, &err);
   if (rc) {

@@ -52,6 +52,15 @@ int validate_config(const mbr_config& c, std::string* err) {
   if (c.frames < 1 || c.frames > 8192) return bad("frames must be in 1..8192");
   if (c.dtype != MBR_F32 && c.dtype != MBR_F16 && c.dtype != MBR_BF16) return bad("unknown dtype");
   if (c.io_layout != MBR_IO_FS_T_C && c.io_layout != MBR_IO_SC_F_T) return bad("unknown io_layout");
+  if (c.zero_dc != 0 && c.zero_dc != 1) return bad("zero_dc must be 0 or 1");
+  if (c.band_bins) {
+    int64_t sum = 0;
+    for (int i = 0; i < c.num_bands; ++i) {
+      if (c.band_bins[i] < 1) return bad("every band of band_bins needs at least one bin");
+      sum += c.band_bins[i];
+    }
+    if (sum != c.n_fft / 2 + 1) return bad("band_bins must add up to n_fft/2 + 1");
+  }
   return MBR_OK;
 }
 
@@ -67,8 +76,10 @@ int build_bands(const mbr_config& cfg, Bands* out, std::string* err) {
   b.channels = S;
   b.bins.assign(NB, {});
   b.count.assign(F, 0);
+  for (int i = 0, k0 = 0; cfg.band_bins && i < NB; k0 += cfg.band_bins[i++])   // explicit table
+    for (int k = k0; k < k0 + cfg.band_bins[i]; ++k) b.bins[i].push_back(k);
   for (int i = 0; i < NB; ++i) {
-    for (int k = 0; k < F; ++k) {
+    for (int k = 0; k < F && !cfg.band_bins; ++k) {
       double hz = (double)k * cfg.sample_rate / cfg.n_fft;
       bool in = pts[i] < hz && hz < pts[i + 2];
       if (i == 0 && k == 0) in = true;
@@ -108,7 +119,7 @@ int build_bands(const mbr_config& cfg, Bands* out, std::string* err) {
       b.inv_slot[2 * p + 1] = slot;
   }
   b.inv_weight.resize((size_t)F * S);
-  for (int p = 0; p < F * S; ++p) b.inv_weight[p] = 1.0f / (float)b.count[p / S];
+  for (int p = 0; p < F * S; ++p) b.inv_weight[p] = (cfg.zero_dc && p / S == 0) ? 0.0f : 1.0f / (float)b.count[p / S];
   *out = std::move(b);
   return MBR_OK;
 }

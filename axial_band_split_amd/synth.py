@@ -57,6 +57,8 @@ class Workload:
     weight_seed: int
     input_seed: int
     hop: int = 441
+    zero_dc: int = 0
+    band_bins: Tuple[int, ...] | None = None   # explicit non-overlapping band table (None: mel)
 
     @property
     def freqs(self) -> int:

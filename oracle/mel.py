@@ -96,6 +96,23 @@ def band_tables(sample_rate: int, n_fft: int, n_mels: int, channels: int) -> Ban
     return BandTables(n_freqs, channels, bins, pairs, widths, counts, inc)
 
 
+def explicit_band_tables(n_fft: int, band_bins, channels: int) -> BandTables:
+    """Contiguous, non-overlapping bands given by their bin counts, low to high, covering every
+    bin once (the band-split table kind; [P2] "62 bands summing to 1025")."""
+    n_freqs = n_fft // 2 + 1
+    band_bins = [int(n) for n in band_bins]
+    if min(band_bins) < 1 or sum(band_bins) != n_freqs:
+        raise ValueError("band bin counts must be >= 1 and add up to n_fft/2 + 1")
+    starts = np.concatenate([[0], np.cumsum(band_bins)[:-1]])
+    inc = np.zeros((len(band_bins), n_freqs), dtype=bool)
+    for i, (k0, n) in enumerate(zip(starts, band_bins)):
+        inc[i, k0:k0 + n] = True
+    bins = [np.nonzero(inc[i])[0].astype(np.int64) for i in range(len(band_bins))]
+    pairs = [(b[:, None] * channels + np.arange(channels)[None, :]).reshape(-1) for b in bins]
+    widths = np.array([2 * channels * len(b) for b in bins], dtype=np.int64)
+    return BandTables(n_freqs, channels, bins, pairs, widths, inc.sum(axis=0).astype(np.int64), inc)
+
+
 def stft_frames(num_samples: int, hop: int) -> int:
     """Frames of a centred STFT ([P1] "The two transformers are not the same shape": 1 + samples/hop)."""
     return 1 + num_samples // hop

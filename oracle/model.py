@@ -64,6 +64,8 @@ class CoreConfig:
     mask_hidden_mult: int = 4
     mask_depth: int = 2
     num_stems: int = 1
+    zero_dc: bool = False                 # the DC bin's masks set to zero ([P5] "zero_dc")
+    band_bins: Tuple[int, ...] | None = None   # explicit non-overlapping band table (None: mel)
 
     @property
     def inner(self) -> int:
@@ -78,6 +80,10 @@ class CoreConfig:
         return self.mask_hidden_mult * self.dim
 
     def tables(self) -> mel.BandTables:
+        if self.band_bins is not None:
+            if len(self.band_bins) != self.num_bands:
+                raise ValueError("band_bins needs one count per band")
+            return mel.explicit_band_tables(self.n_fft, self.band_bins, self.audio_channels)
         return mel.band_tables(self.sample_rate, self.n_fft, self.num_bands, self.audio_channels)
 
 
@@ -315,16 +321,19 @@ def mask_head(x: np.ndarray, cfg: CoreConfig, w: Dict[str, np.ndarray], tables: 
     return out
 
 
-def average(masks: List[np.ndarray], tables: mel.BandTables) -> np.ndarray:
-    """Scatter-add each band's features back to (pair, re/im), divide by the bin's band count.
-    Returns [B, F*S, T, 2]."""
+def average(masks: List[np.ndarray], tables: mel.BandTables, zero_dc: bool = False) -> np.ndarray:
+    """Scatter-add each band's features back to (pair, re/im), divide by the bin's band count;
+    with zero_dc the DC bin's masks are zero.  Returns [B, F*S, T, 2]."""
     B, T, _ = masks[0].shape
     S = tables.channels
     out = np.zeros((B, tables.n_freqs * S, T, 2))
     for m, pairs in zip(masks, tables.pairs):
         out[:, pairs, :, :] += np.transpose(m.reshape(B, T, len(pairs), 2), (0, 2, 1, 3))
     per_pair = np.repeat(tables.counts, S).astype(np.float64)
-    return out / per_pair[None, :, None, None]
+    out = out / per_pair[None, :, None, None]
+    if zero_dc:
+        out[:, :S] = 0.0
+    return out
 
 
 @dataclass
@@ -360,5 +369,5 @@ def forward(spec_in: np.ndarray, cfg: CoreConfig, weights: Sequence[np.ndarray],
         m = mask_head(x, cfg, w, tables, s)
         if taps is not None and s == 0:
             taps.glu = m
-        outs.append(write_output(average(m, tables), cfg.audio_channels, layout))
+        outs.append(write_output(average(m, tables, cfg.zero_dc), cfg.audio_channels, layout))
     return outs[0] if cfg.num_stems == 1 else np.stack(outs, axis=1)

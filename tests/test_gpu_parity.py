@@ -3,6 +3,8 @@
 Bars: relative L2 of the masks <= 1e-4 on the fp32 path and <= 2e-2 on the fp16 / bf16 paths
 (the core's stated tolerances); band and index tables are checked bit-exact on the CPU.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -17,7 +19,8 @@ TOL = {synth.F32: 1e-4, synth.F16: 2e-2, synth.BF16: 2e-2}
 
 def ocfg(w: synth.Workload) -> M.CoreConfig:
     return M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads,
-                        w.dim_head, w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+                        w.dim_head, w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems, bool(w.zero_dc),
+                        w.band_bins)
 
 
 def rel_l2(a, b):
@@ -264,3 +267,39 @@ def test_frame_counts_off_the_presets(frames):
     err = rel_l2(y, M.forward(x, ocfg(w), ws))
     say(f"[frames] T={frames}: rel L2 = {err:.3e}")
     assert err <= TOL[w.dtype]
+
+
+SPLIT_62 = (4,) * 20 + (8,) * 16 + (16,) * 12 + (32,) * 8 + (62,) * 5 + (59,)
+
+
+@pytest.mark.parametrize("dtype,zero_dc", [(synth.F16, 0), (synth.BF16, 1)])
+def test_explicit_band_table_matches_oracle(dtype, zero_dc):
+    """A non-overlapping 62-band table (every bin in one band, no averaging) on the vocals
+    architecture, and the DC bin zeroed."""
+    w = synth.WORKLOADS["t256_fp16"].replace(num_bands=62, band_bins=SPLIT_62, zero_dc=zero_dc, dtype=dtype,
+                                             frames=48, depth=1)
+    say(f"[bands] 62 explicit bands, {synth.DTYPE_NAMES[dtype]}, zero_dc={zero_dc}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    oc = dataclasses.replace(ocfg(w), band_bins=SPLIT_62, zero_dc=bool(zero_dc))
+    ref = M.forward(x, oc, ws)
+    err = rel_l2(y, ref)
+    say(f"[bands] rel L2 = {err:.3e}")
+    assert err <= TOL[dtype]
+    if zero_dc:
+        assert np.all(y[:, :2] == 0.0)
+
+
+def test_zero_dc_on_the_fp32_path():
+    w = synth.WORKLOADS["tiny_fp32"].replace(zero_dc=1)
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, dataclasses.replace(ocfg(w), zero_dc=True), ws)
+    assert np.all(y[:, :2] == 0.0)
+    assert rel_l2(y, ref) <= TOL[synth.F32]

@@ -104,3 +104,34 @@ def test_weight_info_index_out_of_range():
     with pytest.raises(binding.MbrError) as e:
         binding.mbr_core_weight_info(cfg, n)
     assert e.value.code == binding.MBR_E_ARG
+
+
+SPLIT_62 = (4,) * 20 + (8,) * 16 + (16,) * 12 + (32,) * 8 + (62,) * 5 + (59,)
+
+
+@pytest.mark.parametrize("zero_dc", [0, 1])
+def test_explicit_band_table_and_zero_dc_bit_exact_with_oracle(zero_dc):
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(num_bands=62, band_bins=SPLIT_62, zero_dc=zero_dc)
+    got = binding.mbr_core_tables(binding.config(w))
+    t = _oracle_cfg(w, num_bands=62, band_bins=SPLIT_62, zero_dc=bool(zero_dc)).tables()
+    assert got["band_bins"].tolist() == list(SPLIT_62)
+    assert got["gather_pair"].tolist() == np.concatenate(t.pairs).tolist()
+    assert got["bin_count"].tolist() == [1] * 1025
+    inv = got["inv_slot"].reshape(-1, 2)
+    assert inv[:, 1].tolist() == [-1] * (1025 * 2)
+    assert inv[:, 0].tolist() == list(range(1025 * 2))
+    want = np.ones(1025 * 2, dtype=np.float32)
+    if zero_dc:
+        want[:2] = 0.0
+    assert got["inv_weight"].tobytes() == want.tobytes()
+    lib_inv = binding.inventory(binding.config(w))
+    ora_inv = M.inventory(_oracle_cfg(w, num_bands=62, band_bins=SPLIT_62))
+    assert [s for _, s, _ in lib_inv] == [tuple(s) for _, s, _ in ora_inv]
+
+
+@pytest.mark.parametrize("bins", [(500, 524), (0, 1025), (1025, 0), (600, 426)])
+def test_bad_band_tables_are_refused(bins):
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(num_bands=2, band_bins=bins)
+    with pytest.raises(binding.MbrError) as e:
+        binding.mbr_core_weight_count(binding.config(w))
+    assert e.value.code == -2

@@ -1,4 +1,5 @@
 """Pins of the oracle forward: printed sizes, brute force on tiny shapes, closed forms, invariants."""
+import dataclasses
 import json
 import math
 import os
@@ -257,3 +258,42 @@ def test_tiny_forward_runs_in_seconds_and_is_finite():
     x = synth.draw_input(w)
     y = M.forward(x, cfg, ws)
     assert y.shape == (1, 258, 32, 2) and np.isfinite(y).all()
+
+
+# A non-overlapping table with the shape the pages give for the band-split models (62 bands that
+# add up to the 1025 bins of a 2048-point STFT); the widths are this test's own, rising with
+# frequency.
+SPLIT_62 = (4,) * 20 + (8,) * 16 + (16,) * 12 + (32,) * 8 + (62,) * 5 + (59,)
+
+
+def test_explicit_band_table_covers_every_bin_once():
+    assert len(SPLIT_62) == 62 and sum(SPLIT_62) == 1025
+    t = M.CoreConfig(44100, 2048, 2, 62, 384, 1, 8, 64, band_bins=SPLIT_62).tables()
+    assert t.counts.tolist() == [1] * 1025
+    assert np.concatenate(t.bins).tolist() == list(range(1025))
+    assert t.widths.tolist() == [4 * n for n in SPLIT_62]
+    assert t.pairs[1].tolist() == [8, 9, 10, 11, 12, 13, 14, 15]     # bins 4..7, stereo interleaved
+    with pytest.raises(ValueError):
+        M.CoreConfig(44100, 2048, 2, 2, 384, 1, 8, 64, band_bins=(500, 524)).tables()
+
+
+def test_explicit_bands_average_is_the_inverse_permutation():
+    """With every bin in one band the average only puts features back: gather, then average,
+    returns the input exactly."""
+    cfg = M.CoreConfig(44100, 256, 2, 5, 64, 1, 2, 32, band_bins=(10, 20, 30, 40, 29))
+    t = cfg.tables()
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, t.n_freqs * 2, 3, 2))
+    feats = [np.transpose(x[:, p, :, :], (0, 2, 1, 3)).reshape(2, 3, -1) for p in t.pairs]
+    assert np.array_equal(M.average(feats, t), x)
+
+
+def test_zero_dc_zeroes_only_the_dc_bin():
+    """Constant band masks c/2 (as above) with zero_dc: every bin c/2 except both channels of bin 0."""
+    cfg = dataclasses.replace(_tiny_like(), zero_dc=True)
+    t = cfg.tables()
+    B, T = 2, 3
+    masks = [np.full((B, T, W), 0.367) for W in t.widths.tolist()]
+    y = M.average(masks, t, zero_dc=True)
+    assert np.all(y[:, :2] == 0.0)
+    assert np.allclose(y[:, 2:], 0.367, rtol=0, atol=1e-15)
