@@ -37,6 +37,12 @@ _SIGS = {
                              C.c_int, C.c_int, C.c_void_p]),
     "mbr_k_gemm_variants": (C.c_int, []),
     "mbr_k_gelu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]),
+    "mbr_stft": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    "mbr_istft_workspace_size": (C.c_int64, [C.c_int, C.c_int, C.c_int, C.c_int]),
+    "mbr_istft_masked": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_void_p,
+                                   C.c_void_p, C.c_void_p]),
+    "mbr_separate_workspace_size": (C.c_int64, [C.c_void_p, C.c_int64, C.c_int]),
+    "mbr_separate": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
 }
 KERNEL_KINDS = ("gather", "embed", "norm", "qkv", "attn_time", "attn_band", "out_proj", "ffn1", "ffn2",
                 "mask_hidden", "mask_glu", "average", "block")
@@ -178,6 +184,52 @@ def mbr_k_gelu(x_ptr: int, y_ptr: int, n: int, stream_ptr: int = 0) -> None:
     _check(lib().mbr_k_gelu(C.c_void_p(x_ptr), C.c_void_p(y_ptr), n, C.c_void_p(stream_ptr)))
 
 
+def mbr_stft(wave_ptr: int, channels: int, length: int, n_fft: int, hop: int, spec_ptr: int, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_stft(C.c_void_p(wave_ptr), channels, length, n_fft, hop, C.c_void_p(spec_ptr), C.c_void_p(stream_ptr)))
+
+
+def mbr_istft_workspace_size(channels: int, n_fft: int, frames: int, stems: int) -> int:
+    return _check(lib().mbr_istft_workspace_size(channels, n_fft, frames, stems))
+
+
+def mbr_istft_masked(spec_ptr: int, masks_ptr: int, stems: int, channels: int, length: int, n_fft: int, hop: int,
+                     ws_ptr: int, out_ptr: int, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_istft_masked(C.c_void_p(spec_ptr), C.c_void_p(masks_ptr), stems, channels, length, n_fft, hop,
+                                  C.c_void_p(ws_ptr), C.c_void_p(out_ptr), C.c_void_p(stream_ptr)))
+
+
+def mbr_separate_workspace_size(h, length: int, hop: int) -> int:
+    return _check(lib().mbr_separate_workspace_size(h, length, hop))
+
+
+def mbr_separate(h, wave_ptr: int, length: int, hop: int, ws_ptr: int, out_ptr: int, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_separate(h, C.c_void_p(wave_ptr), length, hop, C.c_void_p(ws_ptr), C.c_void_p(out_ptr),
+                              C.c_void_p(stream_ptr)))
+
+
+def stft(wave, n_fft: int, hop: int, stream=None):
+    """wave: float32 CUDA tensor [channels, length] -> stft_repr [1, F*channels, T, 2]."""
+    torch = _torch()
+    _check_dense(wave)
+    S, L = wave.shape
+    out = torch.empty((1, (n_fft // 2 + 1) * S, 1 + L // hop, 2), dtype=torch.float32, device=wave.device)
+    mbr_stft(wave.data_ptr(), S, L, n_fft, hop, out.data_ptr(), _stream_ptr(stream))
+    return out
+
+
+def istft_masked(spec, masks, channels: int, length: int, n_fft: int, hop: int, stream=None):
+    """spec [1, F*S, T, 2] times masks [stems, F*S, T, 2] -> waves [stems, S, length]."""
+    torch = _torch()
+    _check_dense(spec)
+    _check_dense(masks)
+    stems, T = masks.shape[0], spec.shape[2]
+    ws = torch.empty(mbr_istft_workspace_size(channels, n_fft, T, stems), dtype=torch.uint8, device=spec.device)
+    out = torch.empty((stems, channels, length), dtype=torch.float32, device=spec.device)
+    mbr_istft_masked(spec.data_ptr(), masks.data_ptr(), stems, channels, length, n_fft, hop, ws.data_ptr(),
+                     out.data_ptr(), _stream_ptr(stream))
+    return out
+
+
 def mbr_k_gemm_variants() -> int:
     return lib().mbr_k_gemm_variants()
 
@@ -199,6 +251,13 @@ def _torch():
     if not torch.cuda.is_available():
         raise RuntimeError("no GPU visible: the core runs only on an MI355X (gfx950)")
     return torch
+
+
+def _check_dense(t) -> None:
+    """The C ABI takes raw pointers to dense row-major float32 device arrays."""
+    torch = _torch()
+    if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
+        raise ValueError("expected a contiguous float32 CUDA tensor")
 
 
 def _stream_ptr(stream) -> int:
@@ -250,6 +309,16 @@ class Core:
         n = mbr_core_debug_size(self.handle, batch, stage)
         out = torch.empty(n, dtype=torch.float32, device=x.device)
         mbr_core_forward_debug(self.handle, x.data_ptr(), batch, stage, out.data_ptr(), _stream_ptr(stream))
+        return out
+
+    def separate(self, wave, hop: int, stream=None):
+        """wave: float32 CUDA tensor [channels, length] -> stems [num_stems, channels, length]."""
+        torch = _torch()
+        _check_dense(wave)
+        S, L = wave.shape
+        ws = torch.empty(mbr_separate_workspace_size(self.handle, L, hop), dtype=torch.uint8, device=wave.device)
+        out = torch.empty((self.cfg.num_stems, S, L), dtype=torch.float32, device=wave.device)
+        mbr_separate(self.handle, wave.data_ptr(), L, hop, ws.data_ptr(), out.data_ptr(), _stream_ptr(stream))
         return out
 
     def profile(self, x, out, stream=None):

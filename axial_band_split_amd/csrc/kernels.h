@@ -178,6 +178,26 @@ struct BlockLaunch {
                             // split_from * 128 go 32 to a block, split over its waves by hidden chunk
 };
 bool block_supported(int dtype, int D, int I, int FF);
+
+// Geometry of the STFT / inverse STFT of a track cut into chunks (k_stft.hip).  A single signal is
+// one chunk of its own length with no pad and no fades.
+struct StftGeom {
+  const float* wave;        // [S][L] track
+  int32_t S, n_fft, hop, T; // channels, transform size, hop, frames per chunk (1 + chunk / hop)
+  int32_t chunk0;           // first chunk of the current group
+  int32_t no_fade;          // 1: every chunk weight 1 (a single signal)
+  int64_t L, Lp, pad;       // track length, padded length, reflect pad on each side
+  int64_t chunk, stride;    // chunk length and stride in samples
+};
+bool stft_supported(int n_fft);
+hipError_t launch_stft(const StftGeom& G, int ngroup, float* spec, hipStream_t stream);
+hipError_t launch_istft_frames(const StftGeom& G, int ngroup, const float* spec, const float* masks, int stems,
+                               float* frames, hipStream_t stream);
+hipError_t launch_ola(const StftGeom& G, const float* frames, int stems, int ngroup, int64_t lo, int64_t hi,
+                      float* out, float* counter, hipStream_t stream);
+hipError_t launch_finish(const StftGeom& G, int stems, const float* out, const float* counter, float* dst,
+                         hipStream_t stream);
+hipError_t launch_fill0(float* p, int64_t n, hipStream_t stream);
 int64_t block_stream_elems(int D, int I, int FF);
 hipError_t launch_block(const BlockLaunch& L, hipStream_t stream);
 

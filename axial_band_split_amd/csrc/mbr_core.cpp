@@ -1028,6 +1028,125 @@ int64_t mbr_core_device_bytes(const mbr_core* c) {
   return (int64_t)(c->w_bytes + c->f_bytes + c->ws_bytes);
 }
 
+// ---- around the core ------------------------------------------------------------------
+int mbr_stft(const float* wave, int channels, int64_t length, int n_fft, int hop, float* spec, hipStream_t stream) {
+  if (!wave || !spec) return fail(MBR_E_ARG, "NULL argument");
+  if (channels < 1 || length < 2 || !stft_supported(n_fft) || hop < 1 || hop > n_fft / 2)
+    return fail(MBR_E_ARG, "stft: channels >= 1, length >= 2, n_fft a power of two in 16..4096, 1 <= hop <= n_fft/2");
+  StftGeom G{};
+  G.wave = wave;
+  G.S = channels;
+  G.n_fft = n_fft;
+  G.hop = hop;
+  G.T = (int32_t)(1 + length / hop);
+  G.no_fade = 1;
+  G.L = G.Lp = G.chunk = G.stride = length;
+  HIP_TRY(launch_stft(G, 1, spec, stream));
+  return MBR_OK;
+}
+
+int64_t mbr_istft_workspace_size(int channels, int n_fft, int frames, int stems) {
+  if (channels < 1 || frames < 1 || stems < 1 || !stft_supported(n_fft)) return fail(MBR_E_ARG, "bad sizes");
+  return (int64_t)stems * channels * frames * n_fft * 4;
+}
+
+int mbr_istft_masked(const float* spec, const float* masks, int stems, int channels, int64_t length, int n_fft,
+                     int hop, void* workspace, float* out, hipStream_t stream) {
+  if (!spec || !masks || !workspace || !out) return fail(MBR_E_ARG, "NULL argument");
+  if (channels < 1 || stems < 1 || length < 2 || !stft_supported(n_fft) || hop < 1 || hop > n_fft / 2)
+    return fail(MBR_E_ARG, "istft: bad sizes");
+  StftGeom G{};
+  G.S = channels;
+  G.n_fft = n_fft;
+  G.hop = hop;
+  G.T = (int32_t)(1 + length / hop);
+  G.no_fade = 1;
+  G.L = G.Lp = G.chunk = G.stride = length;
+  float* frames = (float*)workspace;
+  HIP_TRY(launch_istft_frames(G, 1, spec, masks, stems, frames, stream));
+  HIP_TRY(launch_fill0(out, (int64_t)stems * channels * length, stream));
+  HIP_TRY(launch_ola(G, frames, stems, 1, 0, length, out, nullptr, stream));
+  return MBR_OK;
+}
+
+namespace {
+struct SepPlan {
+  StftGeom G{};
+  int n_chunks = 0, group = 0, stems = 0;
+  size_t o_spec = 0, o_masks = 0, o_frames = 0, o_out = 0, o_cnt = 0, bytes = 0;
+};
+
+int plan_separation(const mbr_core* c, int64_t length, int hop, SepPlan* P) {
+  const mbr_config& cfg = c->cfg;
+  if (cfg.io_layout != MBR_IO_FS_T_C) return fail(MBR_E_ARG, "separate: the core must use MBR_IO_FS_T_C");
+  if (!stft_supported(cfg.n_fft) || hop < 1 || hop > cfg.n_fft / 2) return fail(MBR_E_ARG, "separate: bad hop / n_fft");
+  const int64_t chunk = (int64_t)(c->T - 1) * hop;
+  if (chunk < 20 || length < 2) return fail(MBR_E_ARG, "separate: the core's frames give a chunk of under 20 samples");
+  StftGeom& G = P->G;
+  G.S = c->bands.channels;
+  G.n_fft = cfg.n_fft;
+  G.hop = hop;
+  G.T = c->T;
+  G.chunk = chunk;
+  G.stride = (int64_t)(chunk * 0.9);
+  const int64_t border = chunk - G.stride;
+  G.pad = length > 2 * border ? border : 0;
+  G.L = length;
+  G.Lp = length + 2 * G.pad;
+  P->n_chunks = (int)((G.Lp + G.stride - 1) / G.stride);
+  P->group = std::min(P->n_chunks, c->Bmax);
+  P->stems = cfg.num_stems;
+  const int64_t F = cfg.n_fft / 2 + 1, spec1 = F * G.S * G.T * 2 * 4;
+  size_t off = 0;
+  auto place = [&](size_t b) {
+    size_t o = (off + 255) / 256 * 256;
+    off = o + b;
+    return o;
+  };
+  P->o_spec = place((size_t)P->group * spec1);
+  P->o_masks = place((size_t)P->group * P->stems * spec1);
+  P->o_frames = place((size_t)P->group * P->stems * G.S * G.T * cfg.n_fft * 4);
+  P->o_out = place((size_t)P->stems * G.S * G.Lp * 4);
+  P->o_cnt = place((size_t)G.Lp * 4);
+  P->bytes = off;
+  return MBR_OK;
+}
+}  // namespace
+
+int64_t mbr_separate_workspace_size(const mbr_core* c, int64_t length, int hop) {
+  if (!c) return fail(MBR_E_ARG, "NULL core");
+  SepPlan P;
+  int rc = plan_separation(c, length, hop, &P);
+  return rc ? rc : (int64_t)P.bytes;
+}
+
+int mbr_separate(mbr_core* c, const float* wave, int64_t length, int hop, void* workspace, float* out,
+                 hipStream_t stream) {
+  if (!c || !wave || !workspace || !out) return fail(MBR_E_ARG, "NULL argument");
+  SepPlan P;
+  int rc = plan_separation(c, length, hop, &P);
+  if (rc) return rc;
+  StftGeom& G = P.G;
+  G.wave = wave;
+  char* ws = (char*)workspace;
+  float *spec = (float*)(ws + P.o_spec), *masks = (float*)(ws + P.o_masks), *frames = (float*)(ws + P.o_frames),
+        *acc = (float*)(ws + P.o_out), *cnt = (float*)(ws + P.o_cnt);
+  HIP_TRY(launch_fill0(acc, (int64_t)P.stems * G.S * G.Lp, stream));
+  HIP_TRY(launch_fill0(cnt, G.Lp, stream));
+  for (int c0 = 0; c0 < P.n_chunks; c0 += P.group) {
+    const int g = std::min(P.group, P.n_chunks - c0);
+    G.chunk0 = c0;
+    HIP_TRY(launch_stft(G, g, spec, stream));
+    rc = run_forward(c, spec, masks, g, stream, -1);
+    if (rc) return rc;
+    HIP_TRY(launch_istft_frames(G, g, spec, masks, P.stems, frames, stream));
+    const int64_t lo = (int64_t)c0 * G.stride, hi = std::min(G.Lp, (int64_t)(c0 + g - 1) * G.stride + G.chunk);
+    HIP_TRY(launch_ola(G, frames, P.stems, g, lo, hi, acc, cnt, stream));
+  }
+  HIP_TRY(launch_finish(G, P.stems, acc, cnt, out, stream));
+  return MBR_OK;
+}
+
 void mbr_core_destroy(mbr_core* c) {
   if (!c) return;
   if (c->wdev) (void)hipFree(c->wdev);

@@ -231,6 +231,53 @@ int mbr_k_gelu(const float* x_dev, float* y_dev, int n, hipStream_t stream);
 /* Device bytes held by the core (weights + workspace). */
 int64_t mbr_core_device_bytes(const mbr_core* core);
 
+/* ---- around the core: STFT, masked inverse STFT, chunked separation ----------------- */
+/*
+ * STFT of a waveform as [P1] "The forward chain" takes it: centred (the signal reflected about its
+ * end samples by n_fft/2 on both sides), periodic Hann window of n_fft, hop `hop`, one-sided.
+ *   wave_dev       [channels][length] float32 device array (read).
+ *   stft_repr_dev  [1][F*channels][T][2] float32 device array (written), F = n_fft/2 + 1,
+ *                  T = 1 + length / hop, pair = f*channels + s, last axis (re, im): the core's
+ *                  MBR_IO_FS_T_C input.
+ * n_fft a power of two in 16..4096, 1 <= hop <= n_fft / 2, length >= 2.  Asynchronous on stream.
+ * Returns MBR_E_ARG on bad sizes, MBR_E_HIP if a launch fails.
+ */
+int mbr_stft(const float* wave_dev, int channels, int64_t length, int n_fft, int hop, float* stft_repr_dev,
+             hipStream_t stream);
+/*
+ * Inverse of mbr_stft after the complex product with masks ([P1] "The forward chain": multiply
+ * the original complex STFT, inverse STFT): out[stem][s] = iSTFT(stft_repr x masks[stem]) of
+ * `length` samples, the windowed overlap-add divided by the summed squared window.
+ *   stft_repr_dev  [1][F*channels][T][2] (mbr_stft's layout), T = 1 + length / hop.
+ *   masks_dev      [stems][F*channels][T][2] (the core's output for one chunk).
+ *   workspace_dev  mbr_istft_workspace_size(channels, n_fft, T, stems) bytes of device memory,
+ *                  owned by the caller; contents need not be initialised and are overwritten.
+ *   out_dev        [stems][channels][length] float32 (written).
+ */
+int64_t mbr_istft_workspace_size(int channels, int n_fft, int frames, int stems);
+int mbr_istft_masked(const float* stft_repr_dev, const float* masks_dev, int stems, int channels, int64_t length,
+                     int n_fft, int hop, void* workspace_dev, float* out_dev, hipStream_t stream);
+/*
+ * Separation of one track by chunks ([P1] "Verified inference hot path", steps 3-9): chunk =
+ * (core frames - 1) * hop samples, stride int(0.9 * chunk), border = chunk - stride; a track
+ * longer than two borders is reflect-padded by one border on each side; each chunk (its tail
+ * reflected when it holds more than half a chunk, else zero-padded) goes STFT -> core -> masks x
+ * STFT -> inverse STFT; the estimates are weighted by linear fades of chunk / 10 (none before the
+ * first chunk, none after the last), summed, divided by the summed fades (at least 1e-8), and the
+ * padding is cropped.  Chunks go through the core max_batch at a time.
+ *   core           created with io_layout MBR_IO_FS_T_C and audio_channels = the track's channels;
+ *                  its n_fft is the STFT's.
+ *   wave_dev       [channels][length] float32.
+ *   workspace_dev  mbr_separate_workspace_size(core, length, hop) bytes, caller-owned, any content.
+ *   out_dev        [stems][channels][length] float32 (written).
+ * The core's frames must give a chunk of at least 20 samples, 1 <= hop <= n_fft / 2.  Returns
+ * MBR_E_ARG on bad sizes or a core of another io_layout, MBR_E_HIP if a launch fails; the work
+ * is asynchronous on `stream` and the workspace must stay allocated until it completes.
+ */
+int64_t mbr_separate_workspace_size(const mbr_core* core, int64_t length, int hop);
+int mbr_separate(mbr_core* core, const float* wave_dev, int64_t length, int hop, void* workspace_dev,
+                 float* out_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

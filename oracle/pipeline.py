@@ -71,7 +71,7 @@ def to_core_input(z: np.ndarray) -> np.ndarray:
     """complex [S, F, T] -> stft_repr [1, F*S, T, 2] (pair = f*S + s)."""
     S, F, T = z.shape
     zz = np.transpose(z, (1, 0, 2)).reshape(F * S, T)
-    return np.stack([zz.real, zz.imag], axis=-1)[None]
+    return np.ascontiguousarray(np.stack([zz.real, zz.imag], axis=-1)[None])
 
 
 def apply_masks(z: np.ndarray, masks: np.ndarray) -> np.ndarray:
