@@ -190,5 +190,23 @@ def input_in_layout(w: Workload, x_fs_t_c: np.ndarray) -> np.ndarray:
     return x_fs_t_c if w.io_layout == IO_FS_T_C else fs_t_c_to_sc_f_t(x_fs_t_c, w.audio_channels)
 
 
+def draw_wave(channels: int, length: int, seed: int = 0) -> np.ndarray:
+    """A synthetic track as float32 [channels, length]: Gaussian noise shaped to a 1/f power
+    spectrum (1/sqrt(f) amplitude above 20 Hz at 44.1 kHz), the channels a common part plus a
+    private one (correlation about 0.8), scaled to an RMS of 0.1."""
+    rng = np.random.default_rng(seed)
+    f = np.maximum(np.fft.rfftfreq(length, 1.0 / 44100.0), 20.0)
+    shape = 1.0 / np.sqrt(f)
+
+    def noise():
+        z = np.fft.rfft(rng.standard_normal(length)) * shape
+        return np.fft.irfft(z, n=length)
+
+    common = noise()
+    x = np.stack([common + 0.5 * noise() for _ in range(channels)])
+    x *= 0.1 / np.sqrt(np.mean(x * x))
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
 def shapes_equal(a: Iterable, b: Iterable) -> bool:
     return [tuple(x) for x in a] == [tuple(x) for x in b]

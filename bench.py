@@ -6,8 +6,9 @@
 A step is one forward of the whole core (band gather and embedding, every axial Transformer, the
 mask head, the mask average) over one batch of seeded synthetic spectra already resident in HBM.
 Prints one JSON line: core audio-seconds per second, the per-kernel device times measured with HIP
-events on the launch stream, the roofline of the dominant kernel and the fp64 CPU oracle timed on
-a bounded sample of the same workload.
+events on the launch stream, the roofline of the dominant kernel, the fp64 CPU oracle timed on
+a bounded sample of the same workload, and (beside the headline figure) the separation of a
+synthetic 60 s stereo track through STFT, core, iSTFT and the chunked overlap-add.
 """
 from __future__ import annotations
 
@@ -93,6 +94,35 @@ def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
             "host_cpus": os.cpu_count(), "blas_threads": threads, "seconds_sampled": t3 - t0}
 
 
+def separation(w: synth.Workload, ws, seconds: float, repeats: int) -> dict:
+    """A whole track through the separation entry point: chunked STFT, the core over all chunks at
+    once (max_batch = the chunk count), masks x STFT, inverse STFT, faded overlap-add.  Input resident
+    in HBM; wall time of `repeats` calls after one warm call, synchronised on both sides."""
+    import torch
+    hop = w.hop
+    L = int(seconds * w.sample_rate)
+    chunk = (w.frames - 1) * hop
+    stride = int(chunk * 0.9)
+    pad = chunk - stride if L > 2 * (chunk - stride) else 0
+    n_chunks = -(-(L + 2 * pad) // stride)
+    cfg = binding.config(w, max_batch=n_chunks)
+    core = binding.Core(cfg, ws)
+    wave = torch.from_numpy(synth.draw_wave(w.audio_channels, L, seed=w.input_seed)).cuda()
+    core.separate(wave, hop)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        y = core.separate(wave, hop)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ok = bool(torch.isfinite(y).all().item())
+    core.close()
+    ms = (t1 - t0) * 1e3 / repeats
+    return {"track_seconds": L / w.sample_rate, "chunk_samples": chunk, "stride_samples": stride, "chunks": n_chunks,
+            "max_batch": n_chunks, "repeats": repeats, "ms_per_track": ms, "audio_s_per_s": L / w.sample_rate / (ms * 1e-3),
+            "finite": ok}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +134,8 @@ def main() -> int:
     ap.add_argument("--batch", type=int, default=0, help="override the chunks per call")
     ap.add_argument("--profile-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-seconds", type=float, default=60.0,
+                    help="also time the separation of a synthetic track of this length (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the core runs on one GPU (no sharding, no "
@@ -186,6 +218,12 @@ def main() -> int:
         log(f"[bench]   {k:12s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:4d} launches"
             + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
 
+    sep = None
+    if args.separate_seconds > 0 and w.io_layout == synth.IO_FS_T_C:
+        sep = separation(w, ws, args.separate_seconds, 5)
+        log(f"[bench] separation of {sep['track_seconds']:.0f} s in {sep['chunks']} chunks: {sep['ms_per_track']:.2f} ms, "
+            f"{sep['audio_s_per_s']:.1f} audio-s/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample) ...")
@@ -208,6 +246,7 @@ def main() -> int:
         "device_ms_per_step": dev_ms,
         "profiled_ms_per_step": (tp1 - tp0) * 1e3 / P,
         "kernels": kernels,
+        "separation": sep,
     }
     core.close()
     print(json.dumps(line), flush=True)

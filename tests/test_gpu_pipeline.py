@@ -106,3 +106,23 @@ def test_separation_matches_oracle_tiny_core(L, stems):
     err = rel_l2(got, want)
     say(f"[separate] rel L2 = {err:.2e}")
     assert got.shape == want.shape and err < 1e-4
+
+
+def test_separation_half_precision_vocals_core_matches_oracle():
+    """The vocals architecture (60 bands, D 384, depth 6) in fp16 at 97 frames (42336-sample chunks):
+    a 100000-sample synthetic track gives three chunks, the last one with a reflected tail, two per
+    core call.  The waveforms against the oracle's separation with its fp64 core on the same weights."""
+    w = synth.WORKLOADS["t256_fp16"].replace(frames=97, batch=2)
+    cfg = binding.config(w)
+    ws = synth.draw_weights(binding.inventory(cfg), w.dtype, seed=w.weight_seed)
+    oc = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads, w.dim_head,
+                      w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+    x = synth.draw_wave(2, 100000, seed=7)
+    say("[separate] vocals fp16, 97 frames, 100000 samples")
+    core = binding.Core(cfg, ws)
+    got = core.separate(torch.from_numpy(x).cuda(), 441).cpu().numpy()
+    core.close()
+    want = P.separate(x.astype(np.float64), lambda spec: M.forward(spec, oc, ws), 2048, 441, 96 * 441, 1)
+    err = rel_l2(got, want)
+    say(f"[separate] rel L2 = {err:.2e}")
+    assert got.shape == want.shape and err < 2e-2
