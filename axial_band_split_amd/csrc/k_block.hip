@@ -25,6 +25,12 @@
 // exactly the order the lanes read them: a stage is copied into LDS by 16-byte direct loads and
 // every fragment read is one conflict-free 16-byte LDS read per lane.  Four waves (128 tokens)
 // share each stage; NS stages are in flight.
+//
+// Whole rounds over the device (one 128-token block per compute unit) run every hidden chunk in
+// each block.  The tokens left after them would leave most compute units idle for a full block's
+// time, so they run in blocks that each take one group of hidden chunks (the out-projection is
+// repeated per group): each block writes its part of the feed-forward sum (plus x1 in group 0),
+// and a small kernel adds the parts, b_2, and applies the two norms.
 #include <type_traits>
 
 #include "kcommon.h"
@@ -108,10 +114,9 @@ struct BlockCfg {
   static constexpr int SB = D * 128;
   static constexpr int R = SB / 4096;               // 16-byte loads per thread per stage
   static constexpr int LDS = NS * SB;               // the ring (b_1 is a static LDS array)
-  static_assert(DT % 3 == 0 && 9 * 16 * 64 * 4 <= NS * SB, "split-block reduction layout");
 };
 
-template <typename T, typename C, bool SPLIT_BLOCKS>
+template <typename T, typename C, bool ALL_CHUNKS>
 __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   typedef typename Frag<T>::type frag;
   constexpr int D = C::D, I = C::I, NS = C::NS, DT = C::DT, NCH = C::NCH, KO = C::KO, NST = C::NST,
@@ -121,12 +126,13 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   __shared__ __attribute__((aligned(16))) float b1s[FF];        // b_1, a separate LDS object
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
-  // Blocks below split_from own 128 tokens (a strip of 32 per wave).  The blocks after them take
-  // the tokens left over from whole rounds over the device one strip each: the four waves share
-  // the strip and split the hidden chunks (wave w runs chunks c = w mod 4), then add their parts.
-  constexpr bool split = SPLIT_BLOCKS;
-  const int64_t token = split ? (int64_t)L.split_from * 128 + (int64_t)blockIdx.x * 32 + (lane & 31)
-                              : (int64_t)blockIdx.x * 128 + w * 32 + (lane & 31);
+  // block = (token group, chunk group q); a wave owns 32 tokens of the group's 128 and runs the
+  // hidden chunks [c0, c0 + n) (n even, at least 2).  With ALL_CHUNKS (the whole rounds) the
+  // block runs every chunk and the trip counts are compile-time constants.
+  const int groups = ALL_CHUNKS ? 1 : L.groups;
+  const int q = ALL_CHUNKS ? 0 : blockIdx.x % groups;
+  const int n = ALL_CHUNKS ? NCH : NCH / groups, c0 = q * n;
+  const int64_t token = (ALL_CHUNKS ? 0 : L.tok0) + (int64_t)(blockIdx.x / groups) * 128 + w * 32 + (lane & 31);
   const bool valid = token < L.tokens;
   // lanes past the last token read the last token's row and store nothing (a token's lanes only
   // ever combine with each other)
@@ -137,23 +143,27 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   __syncthreads();
 
   const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform: LDS bases stay scalar
-  auto issue = [&](int st) {
-    const char* g = stream + (size_t)st * SB + tid * 16;
-    char* l = smem + (st % NS) * SB + wu * 1024;
+  // Step i of the block reads stream stage i (out-projection, i < KO) or KO + c0 + (i - KO) (the
+  // stage holding W_1 of chunk c0 + i - KO and W_2 of the chunk two before it) into ring slot i % NS.
+  const int nsteps = KO + n + 2;
+  static_assert(NST == KO + NCH + 2, "stream length");
+  auto issue = [&](int i) {
+    const char* g = stream + (size_t)(i < KO ? i : i + c0) * SB + tid * 16;
+    char* l = smem + (i % NS) * SB + wu * 1024;
 #pragma unroll
     for (int r = 0; r < R; ++r) dma16(g + r * 4096, l + r * 4096);
   };
-  // stage st is complete once at most (stages issued after it) * R loads are outstanding (the
+  // step i's stage is complete once at most (stages issued after it) * R loads are outstanding (the
   // attention-output loads issued in between only make this wait longer than needed).  The next
   // stage is requested once this one's LDS reads are all issued: its slot was last read in the
   // previous step, which every wave finished before the barrier.
-  auto stage_begin = [&](int st) {
-    if (st + NS - 2 < NST) wait_vm<(NS - 2) * R>();
+  auto stage_begin = [&](int i) {
+    if (i + NS - 2 < nsteps) wait_vm<(NS - 2) * R>();
     else wait_vm<0>();
     block_barrier();
   };
-  auto stage_end = [&](int st) {
-    if (st + NS - 1 < NST) issue(st + NS - 1);
+  auto stage_end = [&](int i) {
+    if (i + NS - 1 < nsteps) issue(i + NS - 1);
   };
 
 #pragma unroll
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   for (int s = 0; s < D / 16; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) xb[s][e] = cvt<T>(acc[s >> 1][8 * (s & 1) + e] * r1);
-  if (split && w != 0) {   // only wave 0 carries x1; the others accumulate their hidden chunks' part
+  if (q != 0) {   // only chunk group 0 carries x1; the others accumulate their chunks' part
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -217,12 +227,11 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   // vector work fills the shadows of the products.  The loop is unrolled by two so the hidden-tile
   // registers alternate without copies.  (A chain of dependent products on one accumulator runs
   // at full rate on this matrix core, so the first product needs only one.)
-  constexpr bool SPLIT = false;
   constexpr int N1 = D / 16, N2 = 2 * DT;
-  f32x16 hA0{}, hA1{}, hB0{}, hB1{};
+  f32x16 hA{}, hB{};
   frag gA0{}, gA1{}, gB0{}, gB1{};
-  auto step = [&](auto do1_, auto dog_, auto do2_, const char* sl, int c, f32x16& n0, f32x16& n1,
-                  const f32x16& o0, const f32x16& o1, frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
+  auto step = [&](auto do1_, auto dog_, auto do2_, const char* sl, int c, f32x16& n0, const f32x16& o0,
+                  frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
     constexpr bool do1 = decltype(do1_)::value, dog = decltype(dog_)::value, do2 = decltype(do2_)::value;
     constexpr int NA = do1 ? N1 : 0, NB = do2 ? N2 : 0, G = (NA + NB) / GS;
     if constexpr (do1) {
@@ -233,10 +242,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
       for (int j = 0; j < 4; ++j) {
         const f32x4 b = *(const f32x4*)(bb + 8 * j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          n0[4 * j + i] = b[i];
-          if constexpr (SPLIT) n1[4 * j + i] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i) n0[4 * j + i] = b[i];
       }
     }
     // second-product fragment k = f - NA: tile k % DT, K step k / DT (consecutive products go to
@@ -247,8 +253,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     };
     auto mm = [&](int f, const frag& a) {
       if (f < NA) {
-        if (SPLIT && (f & 1)) mma32(n1, a, xb[f]);
-        else mma32(n0, a, xb[f]);
+        mma32(n0, a, xb[f]);
       } else {
         const int k = f - NA;
         mma32(acc[k % DT], a, (k / DT) ? us1 : us0);
@@ -261,10 +266,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
       if constexpr (dog) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (G == 0 || 1 + v * G / 16 == g) {
-            const float y = SPLIT ? o0[v] + o1[v] : o0[v];
-            (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu_erf(y));
-          }
+          if (G == 0 || 1 + v * G / 16 == g) (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu_erf(o0[v]));
       }
     };
     if constexpr (NA + NB == 0) {
@@ -275,68 +277,43 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   };
   using Y = std::true_type;
   using Nn = std::false_type;
-  auto slot = [&](int c) { return smem + ((KO + c) % NS) * SB + lane * 16; };
-  // step c with the register roles of its parity; in a split block, wave w does only the part of
-  // the step that belongs to its chunks (first product of c, GELU of c-1 or second product of
-  // c-2, whichever is w's; the block still meets at every stage)
-  auto run = [&](auto d1, auto dg, auto d2, int c, f32x16& n0, f32x16& n1, const f32x16& o0, const f32x16& o1,
-                 frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
-    constexpr bool D1 = decltype(d1)::value, DG = decltype(dg)::value, D2 = decltype(d2)::value;
-    const char* sl = slot(c);
-    if constexpr (!split) {
-      step(d1, dg, d2, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
-    } else {
-      const int sel = (c - w) & 3;
-      if (D1 && sel == 0) step(Y{}, Nn{}, Nn{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
-      else if (DG && sel == 1) step(Nn{}, Y{}, Nn{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
-      else if (D2 && sel == 2) step(Nn{}, Nn{}, Y{}, sl, c, n0, n1, o0, o1, mk0, mk1, us0, us1);
-    }
+  // local step j (chunk c0 + j's first product, the GELU of the chunk before it, the second
+  // product of the chunk two before it) with the register roles of its parity
+  auto run = [&](auto d1, auto dg, auto d2, int j, f32x16& n0, const f32x16& o0, frag& mk0, frag& mk1,
+                 const frag& us0, const frag& us1) {
+    const char* sl = smem + ((KO + j) % NS) * SB + lane * 16;
+    step(d1, dg, d2, sl, c0 + j, n0, o0, mk0, mk1, us0, us1);
   };
-  // c = 0, 1
+  // j = 0, 1
   stage_begin(KO);
-  run(Y{}, Nn{}, Nn{}, 0, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
+  run(Y{}, Nn{}, Nn{}, 0, hA, hB, gA0, gA1, gB0, gB1);
   stage_end(KO);
   stage_begin(KO + 1);
-  run(Y{}, Y{}, Nn{}, 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
+  run(Y{}, Y{}, Nn{}, 1, hB, hA, gA0, gA1, gB0, gB1);
   stage_end(KO + 1);
-  for (int c = 2; c < NCH; c += 2) {
-    stage_begin(KO + c);
-    run(Y{}, Y{}, Y{}, c, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
-    stage_end(KO + c);
-    stage_begin(KO + c + 1);
-    run(Y{}, Y{}, Y{}, c + 1, hB0, hB1, hA0, hA1, gA0, gA1, gB0, gB1);
-    stage_end(KO + c + 1);
+  for (int j = 2; j < n; j += 2) {
+    stage_begin(KO + j);
+    run(Y{}, Y{}, Y{}, j, hA, hB, gB0, gB1, gA0, gA1);
+    stage_end(KO + j);
+    stage_begin(KO + j + 1);
+    run(Y{}, Y{}, Y{}, j + 1, hB, hA, gA0, gA1, gB0, gB1);
+    stage_end(KO + j + 1);
   }
-  stage_begin(KO + NCH);
-  run(Nn{}, Y{}, Y{}, NCH, hA0, hA1, hB0, hB1, gB0, gB1, gA0, gA1);
-  stage_end(KO + NCH);
-  stage_begin(KO + NCH + 1);
-  run(Nn{}, Nn{}, Y{}, NCH + 1, hA0, hA1, hB0, hB1, gA0, gA1, gB0, gB1);
+  stage_begin(KO + n);
+  run(Nn{}, Y{}, Y{}, n, hA, hB, gB0, gB1, gA0, gA1);
+  stage_end(KO + n);
+  stage_begin(KO + n + 1);
+  run(Nn{}, Nn{}, Y{}, n + 1, hA, hB, gA0, gA1, gB0, gB1);
 
-  if constexpr (split) {
-    // wave 0 adds the other waves' parts, three tiles per wave at a time through the (now idle)
-    // ring: lane-consecutive floats, [wave-1][tile][v][lane]
-    float* red = (float*)smem;
+  if (!ALL_CHUNKS && groups > 1) {   // this group's part of x2 - b_2, for the reduction kernel
+    if (!valid) return;
+    float* pw = L.part + ((int64_t)q * (L.tokens - L.tok0) + (token - L.tok0)) * D + 4 * h;
 #pragma unroll
-    for (int p = 0; p < DT / 3; ++p) {
-      block_barrier();
-      if (w != 0) {
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) red[(((w - 1) * 3 + q) * 16 + v) * 64 + lane] = acc[3 * p + q][v];
-      }
-      __syncthreads();
-      if (w == 0) {
-#pragma unroll
-        for (int u = 0; u < 3; ++u)
-#pragma unroll
-          for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[3 * p + q][v] += red[((u * 3 + q) * 16 + v) * 64 + lane];
-      }
-    }
-    if (w != 0) return;
+      for (int j = 0; j < 4; ++j)
+        *(float4*)(pw + 32 * t + 8 * j) = make_float4(acc[t][4 * j], acc[t][4 * j + 1], acc[t][4 * j + 2], acc[t][4 * j + 3]);
+    return;
   }
 
   // ---- x2 = acc + b_2;  x3 = RMSNorm_out(x2) -> X;  XH = x3 normalised (or x3)
@@ -387,26 +364,93 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     }
 }
 
+// x2 = b_2 + the chunk groups' parts (group 0 holds x1), then the epilogue of block_kernel:
+// x3 = RMSNorm_out(x2) -> X, XH = x3 normalised (or x3).  One wave per token, lane l holding
+// columns 2l, 2l + 1 of each 128-column slice.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void block_reduce_kernel(BlockLaunch L) {
+  constexpr int P = D / 128;
+  const int lane = threadIdx.x & 63;
+  const int64_t ntail = (int64_t)L.tokens - L.tok0;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= ntail) return;
+  float2 x[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) x[k] = *(const float2*)(L.b2 + 128 * k + 2 * lane);
+#pragma unroll 8
+  for (int q = 0; q < L.groups; ++q) {
+    const float* pr = L.part + ((int64_t)q * ntail + r) * D + 2 * lane;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const float2 v = *(const float2*)(pr + 128 * k);
+      x[k].x += v.x;
+      x[k].y += v.y;
+    }
+  }
+  auto wave_sum = [](float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+  };
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < P; ++k) ss = fmaf(x[k].y, x[k].y, fmaf(x[k].x, x[k].x, ss));
+  const float r2 = 1.0f / fmaxf(sqrtf(wave_sum(ss)), kNormEps);
+  float ss3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const float2 g = *(const float2*)(L.gout + 128 * k + 2 * lane);
+    x[k].x *= r2 * g.x;
+    x[k].y *= r2 * g.y;
+    ss3 = fmaf(x[k].y, x[k].y, fmaf(x[k].x, x[k].x, ss3));
+  }
+  const float r3 = L.xh_norm ? sqrtf((float)D) / fmaxf(sqrtf(wave_sum(ss3)), kNormEps) : 1.0f;
+  const int64_t token = L.tok0 + r;
+  float* xw = L.X + token * D + 2 * lane;
+  T* hw = (T*)L.XH + token * D + 2 * lane;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    *(float2*)(xw + 128 * k) = x[k];
+    hw[128 * k] = cvt<T>(x[k].x * r3);
+    hw[128 * k + 1] = cvt<T>(x[k].y * r3);
+  }
+}
+
+// chunk groups per 128-token group of the tail: the most that keep the tail within one round
+int tail_groups(int64_t tail_blocks, int ncu) {
+  int g = 1;
+  for (int cand : {2, 3, 4, 6, 8, 12, 24})
+    if (tail_blocks * cand <= ncu) g = cand;
+  return g;
+}
+
 template <typename T, typename C>
-hipError_t launch_t(const BlockLaunch& L, hipStream_t stream) {
-  // the last 128-token block may be partial only when no strips follow it
-  if (L.split_from < 0 || (int64_t)L.split_from * 128 >= (int64_t)L.tokens + 128) return hipErrorInvalidValue;
-  // blocks of 128 tokens, then one 32-token strip per block for the rest
-  if (L.split_from > 0) {
-    hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((block_kernel<T, C, false>), dim3(L.split_from), dim3(256), C::LDS, stream, L);
+hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
+  static_assert(C::NCH % 24 == 0, "every group count splits the hidden chunks into even runs");
+  if (L0.ncu < 1 || L0.tokens < 1) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, true>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t round = (int64_t)128 * L0.ncu, rest = L0.tokens % round;
+  BlockLaunch L = L0;
+  if (L0.tokens >= round) {   // whole rounds: 128 tokens and every hidden chunk to a block
+    L.tok0 = 0;
+    L.groups = 1;
+    const BlockLaunch Lm = [&] { BlockLaunch m = L; m.tokens = (int32_t)(L0.tokens - rest); return m; }();
+    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3((unsigned)(Lm.tokens / 128)), dim3(256), C::LDS, stream, Lm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t rest = (int64_t)L.tokens - (int64_t)L.split_from * 128;
-  const int strips = rest > 0 ? (int)((rest + 31) / 32) : 0;
-  if (strips > 0) {
-    hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, true>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3(strips), dim3(256), C::LDS, stream, L);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if (rest == 0) return hipSuccess;
+  const int64_t tb = (rest + 127) / 128;
+  L.tok0 = L0.tokens - rest;
+  L.groups = tail_groups(tb, L0.ncu);
+  if (L.groups > 1 && (!L.part || (size_t)L.groups * rest * C::D * 4 > block_part_bytes(C::D, L0.tokens, L0.ncu)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((block_kernel<T, C, false>), dim3((unsigned)(tb * L.groups)), dim3(256), C::LDS, stream, L);
+  if ((e = hipGetLastError()) != hipSuccess || L.groups == 1) return e;
+  hipLaunchKernelGGL((block_reduce_kernel<T, C::D>), dim3((unsigned)((rest + 3) / 4)), dim3(256), 0, stream, L);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -421,6 +465,11 @@ hipError_t launch_dt(const BlockLaunch& L, hipStream_t stream) {
 // separate products.
 bool block_supported(int dtype, int D, int I, int FF) {
   return dtype != DT_F32 && FF == 4 * D && I == 512 && D == 384;
+}
+
+size_t block_part_bytes(int D, int64_t tokens, int ncu) {
+  const int64_t tail = std::min<int64_t>((int64_t)128 * ncu, 24 * ((tokens + 127) / 128 * 128));
+  return (size_t)tail * D * 4;
 }
 
 int64_t block_stream_elems(int D, int I, int FF) {

@@ -174,9 +174,13 @@ struct BlockLaunch {
   void* XH;                 // [tokens][D] 16-bit copy for the next product
   int32_t tokens, D, I;
   int32_t xh_norm;          // 1: XH = x3 / |x3| * sqrt(D); 0: XH = x3
-  int32_t split_from;       // blocks [0, split_from) take 128 tokens each; the tokens after
-                            // split_from * 128 go 32 to a block, split over its waves by hidden chunk
+  int32_t ncu;              // compute units: a round is one 128-token block per compute unit
+  float* part;              // block_part_bytes(D, tokens, ncu) bytes: partial sums of the tail
+  // set by launch_block for each of its launches
+  int64_t tok0;             // first token of the launch
+  int32_t groups;           // hidden-chunk groups per 128 tokens (1: a block runs every chunk)
 };
+size_t block_part_bytes(int D, int64_t tokens, int ncu);
 bool block_supported(int dtype, int D, int I, int FF);
 
 // Geometry of the STFT / inverse STFT of a track cut into chunks (k_stft.hip).  A single signal is

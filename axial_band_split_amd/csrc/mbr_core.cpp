@@ -134,6 +134,7 @@ struct mbr_core {
   size_t ws_bytes = 0, w_bytes = 0, f_bytes = 0;
   float* X = nullptr;
   void* XH = nullptr;
+  float* part = nullptr;              // fused post-attention kernel: partial sums of the last tokens
   float* gates = nullptr;
   void* U = nullptr;
   void *qt = nullptr, *kt = nullptr, *vt = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
@@ -462,6 +463,7 @@ int alloc_workspace(mbr_core* c) {
          oH1 = place(NT * std::max(c->FF, c->MH) * esz), oH2 = place(NT * c->MH * esz),
          oM = place((size_t)c->cfg.num_stems * BT * c->total * 4);
   size_t oSA = place(NT * kSsStride * 4), oSB = place(NT * kSsStride * 4), oSC = place(NT * kSsStride * 4);
+  size_t oP = place(c->use_block ? block_part_bytes(c->D, (int64_t)NT, c->ncu) : 0);
   c->ws_bytes = off;
   hipError_t e = hipMalloc(&c->ws, off);
   if (e != hipSuccess) return fail(MBR_E_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
@@ -484,6 +486,7 @@ int alloc_workspace(mbr_core* c) {
   c->ssA = (float*)(b + oSA);
   c->ssB = (float*)(b + oSB);
   c->ssC = (float*)(b + oSC);
+  c->part = (float*)(b + oP);
   return MBR_OK;
 }
 
@@ -623,13 +626,8 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
 
     const bool last = t == ntr - 1;
     if (c->use_block) {
-      // The fused kernel holds one group of 128 tokens per compute unit at a time: whole rounds
-      // over the device go 128 tokens to a block.  The rest go 32 to a block (each such block
-      // streams all the weights for a quarter of the tokens, about half a round's time) when they
-      // fit on the device at once, else they take one more, partial round of 128-token blocks.
-      const int64_t round = (int64_t)128 * c->ncu;
-      const int64_t rest_strips = ((int64_t)NT % round + 31) / 32;
-      const int64_t full = (int64_t)NT / round * round + (rest_strips > c->ncu ? (int64_t)NT % round : 0);
+      // one 128-token group per compute unit at a time; the launch splits the hidden chunks of the
+      // tokens after the last whole round over several blocks
       BlockLaunch bl{};
       bl.dtype = dt;
       bl.O = c->O;
@@ -643,7 +641,8 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
       bl.D = c->D;
       bl.I = c->I;
       bl.xh_norm = last ? 0 : 1;
-      bl.split_from = (int32_t)((full + 127) / 128);
+      bl.ncu = c->ncu;
+      bl.part = c->part;
       LAUNCH(MBR_K_BLOCK, launch_block(bl, s));
       if (stop_stage == 1 + t) return MBR_OK;   // X holds x after the output norm
       continue;

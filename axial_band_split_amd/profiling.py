@@ -53,6 +53,8 @@ def short_name(k: str) -> str:
         blk = re.search(r"BlockCfgI\w+?Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", rest)
         if blk and name.startswith("block"):
             tparts.append(f"D{blk.group(1)}/I{blk.group(2)}/{blk.group(3)}st")
+            if re.search(r"ELb0EEEv", rest):
+                tparts.append("chunk groups")
         dh = re.search(r"Li(\d+)EEEv", rest)
         if dh and name.startswith("attn"):
             tparts.append(f"dh{dh.group(1)}")
