@@ -59,7 +59,8 @@ KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E", "qkv": r"gemm2_kernelIDF16b
               "ffn1": r"gemm2_kernelIDF16b?_?Li2E", "out_proj": r"gemm2_kernelIDF16b?_?Li3E",
               "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
               "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
-              "norm": r"norm", "gather": r"gather", "average": r"average", "block": r"block_kernel"}
+              "norm": r"norm", "gather": r"gather", "average": r"average",
+              "block": r"block_kernel|block_reduce_kernel"}
 MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block")
 HBM_KINDS = ("gather", "average", "attn_band", "norm")
 

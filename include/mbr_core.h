@@ -64,11 +64,12 @@ enum { MBR_KIND_MATRIX = 0, MBR_KIND_BIAS = 1, MBR_KIND_GAMMA = 2 };
  *   io_layout               MBR_IO_FS_T_C: [B, F*S, T, 2] (last axis re, im) ([P3]);
  *                           MBR_IO_SC_F_T: [B, S*2, F, T] (planes L re, L im, R re, R im) ([P4]).
  *   zero_dc                 1: the DC bin's masks are zero (the average gives that bin weight 0,
- *                           [P5] roformer export, "zero_dc"); 0: the plain average ([P1]).
+ *                           the zero_dc option of [P5]'s roformer export); 0: the plain average ([P1]).
  *   band_bins               NULL: Slaney-mel bands.  Else a host array of num_bands bin counts:
  *                           contiguous, non-overlapping bands that cover the F bins in order
- *                           (a band-split table of the kind [P2] describes for the band-split
- *                           models: "62 bands summing to 1025").  Read during the call only.
+ *                           (a band-split table of the kind [P2] "Evaluation record" describes
+ *                           for its BS PolarFormer section: 62 bands over all 1025 bins).  Read
+ *                           during the call only.
  */
 typedef struct mbr_config {
   int32_t sample_rate;

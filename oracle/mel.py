@@ -98,7 +98,8 @@ def band_tables(sample_rate: int, n_fft: int, n_mels: int, channels: int) -> Ban
 
 def explicit_band_tables(n_fft: int, band_bins, channels: int) -> BandTables:
     """Contiguous, non-overlapping bands given by their bin counts, low to high, covering every
-    bin once (the band-split table kind; [P2] "62 bands summing to 1025")."""
+    bin once (the band-split table kind: [P2] "Evaluation record", the BS PolarFormer section, a
+    62-band table over all 1025 bins)."""
     n_freqs = n_fft // 2 + 1
     band_bins = [int(n) for n in band_bins]
     if min(band_bins) < 1 or sum(band_bins) != n_freqs:

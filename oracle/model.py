@@ -64,7 +64,7 @@ class CoreConfig:
     mask_hidden_mult: int = 4
     mask_depth: int = 2
     num_stems: int = 1
-    zero_dc: bool = False                 # the DC bin's masks set to zero ([P5] "zero_dc")
+    zero_dc: bool = False                 # the DC bin's masks set to zero ([P5] export-roformer.py option)
     band_bins: Tuple[int, ...] | None = None   # explicit non-overlapping band table (None: mel)
 
     @property
