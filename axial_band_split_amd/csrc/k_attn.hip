@@ -183,9 +183,12 @@ __global__ __launch_bounds__(256) void attn_time_kernel(AttnLaunch L) {
     const float scale = L.gates[row * L.heads + h] / l;
     T* dst = (T*)L.o + row * I + h * DH + 4 * g4;
 #pragma unroll
-    for (int d = 0; d < DH / 16; ++d)
+    for (int d = 0; d < DH / 16; ++d) {
+      typename Vec4<T>::type o4;   // 4 consecutive dims: one 8-byte (16-byte for fp32) store
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[d * 16 + e] = cvt<T>(oacc[d][c][e] * scale);
+      for (int e = 0; e < 4; ++e) o4[e] = cvt<T>(oacc[d][c][e] * scale);
+      *(typename Vec4<T>::type*)(dst + d * 16) = o4;
+    }
   }
 }
 
@@ -216,12 +219,31 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
     // this wave's V [64 keys][DH] -> V^T [DH][keys] in its own LDS slice
     constexpr int EPC = 16 / (int)sizeof(T);
     constexpr int DCH = DH / EPC;
-    for (int c = lane; c < 64 * DCH; c += 64) {
-      const int r = c / DCH, p = c - r * DCH;
-      const uint4 raw = *(const uint4*)(V + (size_t)r * DH + p * EPC);
-      const T* vals = (const T*)&raw;
+    if constexpr (sizeof(T) == 2) {
+      // four keys at a time: four 16-byte rows in, eight 8-byte LDS writes of (4 keys) x 1 dim out
+      static_assert((64 / 4) * DCH % 64 == 0, "whole passes");
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) *(T*)(vlds + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
+      for (int it = 0; it < (64 / 4) * DCH / 64; ++it) {
+        const int idx = it * 64 + lane, kg = idx / DCH, p = idx - kg * DCH;
+        uint4 raw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] = *(const uint4*)(V + (size_t)(4 * kg + j) * DH + p * EPC);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          typename Vec4<T>::type k4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k4[j] = ((const T*)&raw[j])[e];
+          *(typename Vec4<T>::type*)(vlds + (p * EPC + e) * VROW + 4 * kg * (int)sizeof(T)) = k4;
+        }
+      }
+    } else {
+      for (int c = lane; c < 64 * DCH; c += 64) {
+        const int r = c / DCH, p = c - r * DCH;
+        const uint4 raw = *(const uint4*)(V + (size_t)r * DH + p * EPC);
+        const T* vals = (const T*)&raw;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) *(T*)(vlds + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
+      }
     }
   }
 
@@ -297,9 +319,12 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
     const float scale = L.gates[row * L.heads + h] / lsum[c];
     T* dst = (T*)L.o + row * I + h * DH + 4 * g4;
 #pragma unroll
-    for (int d = 0; d < DH / 16; ++d)
+    for (int d = 0; d < DH / 16; ++d) {
+      typename Vec4<T>::type o4;   // 4 consecutive dims: one 8-byte (16-byte for fp32) store
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[d * 16 + e] = cvt<T>(oacc[d][c][e] * scale);
+      for (int e = 0; e < 4; ++e) o4[e] = cvt<T>(oacc[d][c][e] * scale);
+      *(typename Vec4<T>::type*)(dst + d * 16) = o4;
+    }
   }
 }
 
