@@ -215,54 +215,72 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
   constexpr int VROW = 64 * (int)sizeof(T) + 16;
   __shared__ __attribute__((aligned(16))) char vlds_all[4][DH * VROW];
   char* vlds = vlds_all[wave];
-  {
-    // this wave's V [64 keys][DH] -> V^T [DH][keys] in its own LDS slice
-    constexpr int EPC = 16 / (int)sizeof(T);
-    constexpr int DCH = DH / EPC;
-    if constexpr (sizeof(T) == 2) {
-      // four keys at a time: four 16-byte rows in, eight 8-byte LDS writes of (4 keys) x 1 dim out
-      static_assert((64 / 4) * DCH % 64 == 0, "whole passes");
-#pragma unroll
-      for (int it = 0; it < (64 / 4) * DCH / 64; ++it) {
-        const int idx = it * 64 + lane, kg = idx / DCH, p = idx - kg * DCH;
-        uint4 raw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = *(const uint4*)(V + (size_t)(4 * kg + j) * DH + p * EPC);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          typename Vec4<T>::type k4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) k4[j] = ((const T*)&raw[j])[e];
-          *(typename Vec4<T>::type*)(vlds + (p * EPC + e) * VROW + 4 * kg * (int)sizeof(T)) = k4;
-        }
-      }
-    } else {
-      for (int c = lane; c < 64 * DCH; c += 64) {
-        const int r = c / DCH, p = c - r * DCH;
-        const uint4 raw = *(const uint4*)(V + (size_t)r * DH + p * EPC);
-        const T* vals = (const T*)&raw;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) *(T*)(vlds + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
-      }
-    }
-  }
-
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int DCH = DH / EPC;
   f32x4 s[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) s[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+    // Every load of the wave is issued before the first is used (one memory round trip): V four
+    // keys x 8 dims per lane and pass, then the Q and K fragments of every K step.
+    constexpr int VP = (64 / 4) * DCH / 64;
+    static_assert((64 / 4) * DCH % 64 == 0, "whole passes");
+    uint4 vraw[VP][4];
 #pragma unroll
-  for (int st = 0; st < DSTEPS; ++st) {
-    frag qf[4], kf[4];
+    for (int it = 0; it < VP; ++it) {
+      const int idx = it * 64 + lane, kg = idx / DCH, p = idx - kg * DCH;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = *(const frag*)(Q + (size_t)(c * 16 + l16) * DH + st * KS + g4 * EPF);
+      for (int j = 0; j < 4; ++j) vraw[it][j] = *(const uint4*)(V + (size_t)(4 * kg + j) * DH + p * EPC);
+    }
+    frag qf[DSTEPS][4], kf[DSTEPS][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kf[r] = *(const frag*)(K + (size_t)(r * 16 + l16) * DH + st * KS + g4 * EPF);
+    for (int st = 0; st < DSTEPS; ++st)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int c = 0; c < 4; ++c) {
+        qf[st][c] = *(const frag*)(Q + (size_t)(c * 16 + l16) * DH + st * KS + g4 * EPF);
+        kf[st][c] = *(const frag*)(K + (size_t)(c * 16 + l16) * DH + st * KS + g4 * EPF);
+      }
+    // V [64 keys][DH] -> V^T [DH][keys] in the wave's own LDS slice: (4 keys) x 1 dim per 8-byte write
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mma(s[r][c], kf[r], qf[c]);
+    for (int it = 0; it < VP; ++it) {
+      const int idx = it * 64 + lane, kg = idx / DCH, p = idx - kg * DCH;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        typename Vec4<T>::type k4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) k4[j] = ((const T*)&vraw[it][j])[e];
+        *(typename Vec4<T>::type*)(vlds + (p * EPC + e) * VROW + 4 * kg * (int)sizeof(T)) = k4;
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mma(s[r][c], kf[st][r], qf[st][c]);
+  } else {
+    // this wave's V [64 keys][DH] -> V^T [DH][keys] in its own LDS slice
+    for (int c = lane; c < 64 * DCH; c += 64) {
+      const int r = c / DCH, p = c - r * DCH;
+      const uint4 raw = *(const uint4*)(V + (size_t)r * DH + p * EPC);
+      const T* vals = (const T*)&raw;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) *(T*)(vlds + (p * EPC + e) * VROW + r * (int)sizeof(T)) = vals[e];
+    }
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) {
+      frag qf[4], kf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[c] = *(const frag*)(Q + (size_t)(c * 16 + l16) * DH + st * KS + g4 * EPF);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kf[r] = *(const frag*)(K + (size_t)(r * 16 + l16) * DH + st * KS + g4 * EPF);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mma(s[r][c], kf[r], qf[c]);
+    }
   }
   float lsum[4];
 #pragma unroll
