@@ -890,7 +890,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->v_ffn2 = 4;
   c->v_out = 4;
   c->v_mask = 4;
-  c->v_glu = 4;
+  c->v_glu = 2;
   c->v_embed = 4;
   c->use_block = block_supported(cfg->dtype, c->D, c->I, c->FF);
   c->kpad.resize(c->NB);
