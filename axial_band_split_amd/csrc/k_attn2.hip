@@ -48,9 +48,6 @@ __device__ __forceinline__ f32x16 mma32c(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void dma16(const char* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
 
 constexpr float kNegBig = -1e30f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the reference max must move
@@ -96,30 +93,31 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 
   // this thread's DMA chunks: K slot c -> key c / KCH, physical chunk c % KCH holds logical chunk
   // (c % KCH) ^ (key % KCH); V^T slot c -> dim c / 8, 8 keys per chunk, same permutation by dim
-  const char* ksrc[KLD];
-  int kdst[KLD];
+  // K [npad][DH] and V^T [DH][npad] of this (sequence, head) as buffers
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kg, (uint32_t)(npad * DH * 2));
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vg, (uint32_t)(npad * DH * 2));
+  int ksrc[KLD], kdst[KLD];
 #pragma unroll
   for (int j = 0; j < KLD; ++j) {
     const int c = j * 256 + threadIdx.x;
     const int row = c / KCH, pc = c % KCH;
-    ksrc[j] = Kg + (size_t)row * KROWB + ((pc ^ (swz8(row) % KCH)) << 4);
+    ksrc[j] = row * KROWB + ((pc ^ (swz8(row) % KCH)) << 4);
     kdst[j] = (j * 256 + w * 64) * 16;
   }
-  const char* vsrc[VLD];
-  int vdst[VLD];
+  int vsrc[VLD], vdst[VLD];
 #pragma unroll
   for (int j = 0; j < VLD; ++j) {
     const int c = j * 256 + threadIdx.x;
     const int row = c >> 3, pc = c & 7;
-    vsrc[j] = Vg + (size_t)row * npad * 2 + ((pc ^ swz8(row)) << 4);
+    vsrc[j] = row * npad * 2 + ((pc ^ swz8(row)) << 4);
     vdst[j] = KBYTES + (j * 256 + w * 64) * 16;
   }
   auto issue = [&](int kt) {
     char* st = lds + (kt & 1) * STAGE;
 #pragma unroll
-    for (int j = 0; j < KLD; ++j) dma16(ksrc[j] + (size_t)kt * KT * KROWB, st + kdst[j]);
+    for (int j = 0; j < KLD; ++j) buffer_dma16(krs, ksrc[j], kt * KT * KROWB, st + kdst[j]);
 #pragma unroll
-    for (int j = 0; j < VLD; ++j) dma16(vsrc[j] + (size_t)kt * KT * 2, st + vdst[j]);
+    for (int j = 0; j < VLD; ++j) buffer_dma16(vrs, vsrc[j], kt * KT * 2, st + vdst[j]);
   };
 
   // q fragments: B operand of S^T = K Q^T; lane holds query q0 + l32, dims 16*ks + 8*g .. +7

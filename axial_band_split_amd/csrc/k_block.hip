@@ -49,14 +49,6 @@ __device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& 
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16 bytes per lane from the buffer at voff (per lane) + soff (uniform) into LDS at lds_wave_base +
-// 16 * lane.  The buffer form, not the global one: with a FLAT-encoded LDS load in flight the
-// compiler has to assume LDS reads may complete out of order and waits for all of them
-// (lgkmcnt(0)) before every use, which serialises the read groups of the pipelined products.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -147,8 +139,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
 
   const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform: LDS bases stay scalar
   // the weight stream as a buffer (NST * SB bytes; loads past the end would read zeros)
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(L.stream), (short)0, NST * SB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(L.stream, NST * SB);
   // Step i of the block reads stream stage i (out-projection, i < KO) or KO + c0 + (i - KO) (the
   // stage holding W_1 of chunk c0 + i - KO and W_2 of the chunk two before it) into ring slot i % NS.
   const int nsteps = KO + n + 2;
@@ -157,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     const int g = (i < KO ? i : i + c0) * SB;
     char* l = smem + (i % NS) * SB + wu * 1024;
 #pragma unroll
-    for (int r = 0; r < R; ++r) dma16(srs, tid * 16, g + r * 4096, l + r * 4096);
+    for (int r = 0; r < R; ++r) buffer_dma16(srs, tid * 16, g + r * 4096, l + r * 4096);
   };
   // step i's stage is complete once at most (stages issued after it) * R loads are outstanding (the
   // attention-output loads issued in between only make this wait longer than needed).  The next

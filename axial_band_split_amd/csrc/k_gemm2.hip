@@ -36,9 +36,6 @@ __device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& 
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-__device__ __forceinline__ void dma16(const char* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima), plus a compiler barrier.
@@ -102,31 +99,34 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
   }
   if (m0 >= M) return;
 
-  // ---- loader: this thread's 16-byte chunks of a stage (global source, wave-uniform LDS target)
-  const char* Ag = (const char*)L.A + (g.a_off0 + g.a_offb * (int64_t)M) * 2;
-  const char* Bg = (const char*)L.B + g.b_off * 2;
+  // ---- loader: this thread's 16-byte chunks of a stage, from buffers over this tile's A rows
+  // and B rows (rows past the end read the last row), into wave-uniform LDS targets
   const int64_t lda_b = (int64_t)g.lda * 2, ldb_b = (int64_t)g.ldb * 2;
-  const char* src[C::LOADS];
-  int dst[C::LOADS];
+  const int arows = min(BM, M - m0), brows = max(1, min(BN, g.N - n0));
+  const __amdgpu_buffer_rsrc_t ars =
+      buffer_rsrc((const char*)L.A + (g.a_off0 + g.a_offb * (int64_t)M) * 2 + (int64_t)m0 * lda_b, (uint32_t)(arows * lda_b));
+  const __amdgpu_buffer_rsrc_t brs =
+      buffer_rsrc((const char*)L.B + g.b_off * 2 + (int64_t)n0 * ldb_b, (uint32_t)(brows * ldb_b));
+  int voff[C::LOADS], dst[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LD; ++j) {
     const int row = (j * NW + w) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(row);
-    src[j] = Ag + (int64_t)min(m0 + row, M - 1) * lda_b + c * 16;
+    voff[j] = (int)(min(row, arows - 1) * lda_b) + c * 16;
     dst[j] = (j * NW + w) * 1024;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LD; ++j) {
     const int row = (j * NW + w) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(row);
-    src[C::A_LD + j] = Bg + (int64_t)min(n0 + row, g.N - 1) * ldb_b + c * 16;
+    voff[C::A_LD + j] = (int)(min(row, brows - 1) * ldb_b) + c * 16;
     dst[C::A_LD + j] = C::A_BYTES + (j * NW + w) * 1024;
   }
   auto issue = [&](int ks) {
     char* base = smem + (ks % NS) * C::STAGE;
-    const int64_t ko = (int64_t)ks * 64;
+    const int ko = ks * 64;
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) dma16(src[j] + ko, base + dst[j]);
+    for (int j = 0; j < C::LOADS; ++j) buffer_dma16(j < C::A_LD ? ars : brs, voff[j], ko, base + dst[j]);
   };
 
   f32x16 acc[TM][2];

@@ -75,4 +75,17 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 
 constexpr float kNormEps = 1e-12f;
 
+// A raw buffer over [base, base + bytes) for the loads below (bytes < 2^31; reads past the end
+// return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from buffer offset voff (per lane) + soff (uniform) into LDS at
+// lds_wave_base + 16 * lane.  The buffer form of the LDS load and not the global one: with a
+// FLAT-encoded load to LDS in flight the compiler must assume LDS reads complete out of order and
+// waits for every one of them (lgkmcnt(0)) before any use, which serialises pipelined reads.
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
 }  // namespace mbr
