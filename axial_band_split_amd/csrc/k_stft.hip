@@ -7,7 +7,7 @@
 //
 //   * one workgroup transforms one frame: the n_fft samples (or the one-sided spectrum, Hermitian-
 //     completed) go into LDS and through a radix-2 Stockham FFT there (log2 n_fft stages, natural
-//     order out, twiddles and window computed once per workgroup in double precision);
+//     order out, twiddles and window computed once per workgroup);
 //   * every index map of the chunking (track reflect pad, chunk tail reflected or zeroed, the STFT's
 //     own centre reflection) is applied while loading, so no padded copy of the track exists;
 //   * the chunks' estimates are combined by a gather over output samples (at most two chunks and
@@ -46,14 +46,15 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
-// twiddles e^{-2 pi i k / N}, k < N/2, and the periodic Hann window, in double precision
+// twiddles e^{-2 pi i k / N}, k < N/2, and the periodic Hann window: single-precision sin / cos
+// of pi x (about one ulp) at arguments that are exact in float (N a power of two)
 __device__ void tables(float2* tw, float* win, int N) {
   for (int k = threadIdx.x; k < N / 2; k += blockDim.x) {
-    double sn, cs;
-    sincospi(-2.0 * k / N, &sn, &cs);
-    tw[k] = make_float2((float)cs, (float)sn);
+    float sn, cs;
+    sincospif(-2.0f * k / N, &sn, &cs);
+    tw[k] = make_float2(cs, sn);
   }
-  for (int i = threadIdx.x; i < N; i += blockDim.x) win[i] = (float)(0.5 - 0.5 * cospi(2.0 * i / N));
+  for (int i = threadIdx.x; i < N; i += blockDim.x) win[i] = 0.5f - 0.5f * cospif(2.0f * i / N);
 }
 
 // radix-2 Stockham FFT of N points from a into b (result in the returned buffer); inverse: e^{+i}
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void istft_frames_kernel(StftGeom G, const flo
   for (int i = threadIdx.x; i < N; i += blockDim.x) dst[i] = y[i].x * inv * win[i];
 }
 
-__device__ __forceinline__ float hann_at(int i, int N) { return (float)(0.5 - 0.5 * cospi(2.0 * i / N)); }
+__device__ __forceinline__ float hann_at(int i, int N) { return 0.5f - 0.5f * cospif(2.0f * i / N); }
 
 // fade window of chunk c at local position j (linear, endpoints included; none at the track ends)
 __device__ __forceinline__ float fade_at(const StftGeom& G, int c, int64_t j) {
