@@ -324,8 +324,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
       for (int e = 0; e < 8; ++e) bvals[e] = bias ? bias[cbase + c8 + e] : 0.f;
       // sequence / position of this lane's first row; later rows step by 8 (at most one wrap
       // per step when a sequence is at least 8 long, loops otherwise)
-      int seq = 0, pos = 0, wrap = 1;
+      int seqs[4] = {0, 0, 0, 0}, poss[4] = {0, 0, 0, 0};
+      float4 csv[4], snv[4];
       if constexpr (EPI == EPI_QKV) {
+        int seq, pos, wrap;
         const int r0 = rbase + (lane >> 3);
         if (qa.axis == 0) {
           wrap = qa.frames;
@@ -336,13 +338,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
           pos = r0 / wrap;
           seq = r0 - pos * wrap;
         }
-      }
-#pragma unroll 2
-      for (int it = 0; it < 4; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int row = rbase + r;
-        const float sc = __shfl(sc_mine, r, 64);
-        if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
           if (it > 0) {
             // advance the (seq, pos) pair by 8 rows
             if (qa.axis == 0) {
@@ -353,7 +350,25 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
               while (seq >= wrap) { seq -= wrap; ++pos; }
             }
           }
+          seqs[it] = seq;
+          poss[it] = pos;
         }
+        // the rotary factors of the four rows, all loaded before the first is used
+        if (which < 2)
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int pr = rbase + it * 8 + (lane >> 3) < M ? poss[it] : 0;
+            csv[it] = *(const float4*)(qa.cos + pr * (qa.dh >> 1) + (d0 >> 1));
+            snv[it] = *(const float4*)(qa.sin + pr * (qa.dh >> 1) + (d0 >> 1));
+          }
+      }
+      constexpr int kRowUnroll = EPI == EPI_QKV ? 4 : 2;   // QKV: its per-row arrays stay in registers
+#pragma unroll kRowUnroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int row = rbase + r;
+        const float sc = __shfl(sc_mine, r, 64);
+        const int seq = seqs[it], pos = poss[it];
         if (row >= M) continue;
         const float4 a0 = *(const float4*)(ep + r * ES + c8);
         const float4 a1 = *(const float4*)(ep + r * ES + c8 + 4);
@@ -374,8 +389,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
             continue;
           }
           if (which < 2) {
-            const float4 cs = *(const float4*)(qa.cos + pos * (qa.dh >> 1) + (d0 >> 1));
-            const float4 sn = *(const float4*)(qa.sin + pos * (qa.dh >> 1) + (d0 >> 1));
+            const float4 cs = csv[it], sn = snv[it];
             const float cc[4] = {cs.x, cs.y, cs.z, cs.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
