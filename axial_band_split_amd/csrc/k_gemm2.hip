@@ -412,7 +412,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
           for (int e = 0; e < 8; ++e) {
             const float xv = v[e] + bvals[e];
             if constexpr (EPI == EPI_GELU) p[e] = cvt<T>(gelu_erf(xv));
-            else if constexpr (EPI == EPI_TANH) p[e] = cvt<T>(tanhf(xv));
+            else if constexpr (EPI == EPI_TANH) p[e] = cvt<T>(tanh_fast(xv));
             else p[e] = cvt<T>(xv);
           }
           *(pack*)(Cp + (int64_t)row * L.ldc + cbase + c8) = p;

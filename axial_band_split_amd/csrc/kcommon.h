@@ -70,6 +70,11 @@ __device__ __forceinline__ float erf_as(float x) {
   const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
   return copysignf(fmaf(-p, e, 1.0f), x);
 }
+// tanh x = 1 - 2 / (e^{2x} + 1): one exponential and one reciprocal (absolute error a few 1e-7,
+// far below the 16-bit rounding of the values it feeds; +-1 at the extremes, where e^{2x} is inf or 0).
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * 2.8853900817779268f));
+}
 // GELU with the error function (x * Phi(x)), as the feed-forward of the core uses it.
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 
