@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(s[r][c][e] - mx);
+        const float p = __builtin_amdgcn_exp2f(s[r][c][e] - mx);
         s[r][c][e] = p;
         sum += p;
       }

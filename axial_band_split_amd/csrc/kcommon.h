@@ -55,7 +55,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// sigma(x) = 1 / (1 + 2^(-x log2 e)) with the hardware exp2 and reciprocal (about 2 ulp; 0 and 1
+// at the extremes, where the exponential is inf or 0)
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
 // erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0, with
 // |error| <= 1.5e-7; odd in z.  One reciprocal, five FMAs and one exponential.
