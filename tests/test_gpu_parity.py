@@ -269,6 +269,35 @@ def test_frame_counts_off_the_presets(frames):
     assert err <= TOL[w.dtype]
 
 
+def _tail_groups(tokens: int, ncu: int = 256) -> int:
+    """Hidden-chunk groups the fused post-attention kernel gives the tokens after its whole rounds
+    of 128 * ncu (the most of 2, 3, 4, 6, 8, 12, 24 that keep them within one round)."""
+    blocks = -(-(tokens % (128 * ncu)) // 128)
+    return max([1] + [g for g in (2, 3, 4, 6, 8, 12, 24) if blocks * g <= ncu])
+
+
+@pytest.mark.parametrize("frames,batch,groups", [(32, 1, 12), (32, 2, 8), (40, 2, 6), (96, 1, 4), (40, 4, 3),
+                                                 (96, 2, 2), (96, 4, 1)])
+def test_fused_kernel_tail_in_every_group_count(frames, batch, groups):
+    """The vocals architecture (one layer, fp16) at token counts whose tail runs in 12, 8, 6, 4, 3, 2
+    and 1 hidden-chunk groups (on a device of 256 compute units): each group's partial sums and the
+    reduction kernel against the oracle."""
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(frames=frames, batch=batch, depth=1)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    got_groups = _tail_groups(w.num_bands * frames * batch, ncu)
+    say(f"[tail] T={frames} B={batch}: {got_groups} chunk groups on {ncu} compute units")
+    if ncu == 256:
+        assert got_groups == groups
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    err = rel_l2(y, M.forward(x, ocfg(w), ws))
+    say(f"[tail] T={frames} B={batch}: rel L2 = {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 SPLIT_62 = (4,) * 20 + (8,) * 16 + (16,) * 12 + (32,) * 8 + (62,) * 5 + (59,)
 
 
