@@ -26,7 +26,7 @@
 // every fragment read is one conflict-free 16-byte LDS read per lane.  Four waves (128 tokens)
 // share each stage; NS stages are in flight.
 //
-// Whole rounds over the device (one 128-token block per compute unit) run every hidden chunk in
+// Whole device passes (one 128-token block per compute unit) run every hidden chunk in
 // each block.  The tokens left after them would leave most compute units idle for a full block's
 // time, so they run in blocks that each take one group of hidden chunks (the out-projection is
 // repeated per group): each block writes its part of the feed-forward sum (plus x1 in group 0),
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
   // block = (token group, chunk group q); a wave owns 32 tokens of the group's 128 and runs the
-  // hidden chunks [c0, c0 + n) (n even, at least 2).  With ALL_CHUNKS (the whole rounds) the
+  // hidden chunks [c0, c0 + n) (n even, at least 2).  With ALL_CHUNKS (the whole passes) the
   // block runs every chunk and the trip counts are compile-time constants.
   const int groups = ALL_CHUNKS ? 1 : L.groups;
   const int q = ALL_CHUNKS ? 0 : blockIdx.x % groups;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(256) void block_reduce_kernel(BlockLaunch L) {
   }
 }
 
-// chunk groups per 128-token group of the tail: the most that keep the tail within one round
+// chunk groups per 128-token group of the tail: the most that keep the tail within one device pass
 int tail_groups(int64_t tail_blocks, int ncu) {
   int g = 1;
   for (int cand : {2, 3, 4, 6, 8, 12, 24})
@@ -429,9 +429,9 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
-  const int64_t round = (int64_t)128 * L0.ncu, rest = L0.tokens % round;
+  const int64_t pass = (int64_t)128 * L0.ncu, rest = L0.tokens % pass;
   BlockLaunch L = L0;
-  if (L0.tokens >= round) {   // whole rounds: 128 tokens and every hidden chunk to a block
+  if (L0.tokens >= pass) {   // whole passes: 128 tokens and every hidden chunk to a block
     L.tok0 = 0;
     L.groups = 1;
     const BlockLaunch Lm = [&] { BlockLaunch m = L; m.tokens = (int32_t)(L0.tokens - rest); return m; }();

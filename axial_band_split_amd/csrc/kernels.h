@@ -174,7 +174,7 @@ struct BlockLaunch {
   void* XH;                 // [tokens][D] 16-bit copy for the next product
   int32_t tokens, D, I;
   int32_t xh_norm;          // 1: XH = x3 / |x3| * sqrt(D); 0: XH = x3
-  int32_t ncu;              // compute units: a round is one 128-token block per compute unit
+  int32_t ncu;              // compute units: a device pass is one 128-token block per compute unit
   float* part;              // block_part_bytes(D, tokens, ncu) bytes: partial sums of the tail
   // set by launch_block for each of its launches
   int64_t tok0;             // first token of the launch

@@ -627,7 +627,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     const bool last = t == ntr - 1;
     if (c->use_block) {
       // one 128-token group per compute unit at a time; the launch splits the hidden chunks of the
-      // tokens after the last whole round over several blocks
+      // tokens after the last whole device pass over several blocks
       BlockLaunch bl{};
       bl.dtype = dt;
       bl.O = c->O;

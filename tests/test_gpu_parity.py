@@ -270,8 +270,8 @@ def test_frame_counts_off_the_presets(frames):
 
 
 def _tail_groups(tokens: int, ncu: int = 256) -> int:
-    """Hidden-chunk groups the fused post-attention kernel gives the tokens after its whole rounds
-    of 128 * ncu (the most of 2, 3, 4, 6, 8, 12, 24 that keep them within one round)."""
+    """Hidden-chunk groups the fused post-attention kernel gives the tokens after its whole device
+    passes of 128 * ncu (the most of 2, 3, 4, 6, 8, 12, 24 that keep them within one pass)."""
     blocks = -(-(tokens % (128 * ncu)) // 128)
     return max([1] + [g for g in (2, 3, 4, 6, 8, 12, 24) if blocks * g <= ncu])
 
