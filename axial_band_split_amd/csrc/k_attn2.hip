@@ -51,6 +51,7 @@ __device__ __forceinline__ f32x16 mma32c(const bf16x8& a, const bf16x8& b, const
 
 constexpr float kNegBig = -1e30f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the reference max must move
+constexpr int kKeysPerTile = 64;   // 128 halves the waits per key but leaves 2 instead of 3 workgroups per CU (slower)
 
 // LDS rows of 128 bytes (8 chunks of 16): chunk c of row r sits in slot c ^ ((r >> 1) & 7), so any
 // 16 consecutive rows read at one chunk cover all 64 banks.
@@ -59,12 +60,14 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 // which puts the 8 probabilities a lane feeds to one P.V step on 8 consecutive keys.
 __device__ __forceinline__ int perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <typename T, int DH>
+template <typename T, int DH, int KT>
 __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
-  constexpr int KT = 64;                     // keys per tile
+  static_assert(KT % 32 == 0, "keys per tile");
+  constexpr int RT = KT / 32;                // 32-key row tiles of S^T per key tile
   constexpr int KROWB = DH * 2;              // bytes per K row
   constexpr int KCH = KROWB / 16;            // 16-byte chunks per K row
-  constexpr int VROWB = KT * 2;              // bytes per V^T row (64 keys)
+  constexpr int VROWB = KT * 2;              // bytes per V^T row (KT keys)
+  constexpr int VCH = VROWB / 16;            // 16-byte chunks per V^T row
   constexpr int KBYTES = KT * KROWB, VBYTES = DH * VROWB;
   constexpr int STAGE = KBYTES + VBYTES;
   constexpr int KLD = KBYTES / (256 * 16), VLD = VBYTES / (256 * 16);   // loads per thread per stage
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 #pragma unroll
   for (int j = 0; j < VLD; ++j) {
     const int c = j * 256 + threadIdx.x;
-    const int row = c >> 3, pc = c & 7;
+    const int row = c / VCH, pc = c % VCH;
     vsrc[j] = row * npad * 2 + ((pc ^ swz8(row)) << 4);
     vdst[j] = KBYTES + (j * 256 + w * 64) * 16;
   }
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     if (kt + 1 < ntiles) issue(kt + 1);
     const char* st = lds + (kt & 1) * STAGE;
 
-    f32x16 s[2];
+    f32x16 s[RT];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RT; ++r) {
       const int row = r * 32 + perm(l32);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     }
     if (kt == ntiles - 1 && (n & (KT - 1))) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kt * KT + r * 32 + perm(8 * (v >> 2) + 4 * g + (v & 3));
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     }
     float mx = kNegBig;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[r][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -193,10 +196,10 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) negm[v] = -mref;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) s[r] -= up;
+      for (int r = 0; r < RT; ++r) s[r] -= up;
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2 * RT; ++t) {
       const int r = t >> 1, hv = (t & 1) * 8;
       frag pf;
 #pragma unroll
@@ -232,8 +235,8 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 template <typename T>
 hipError_t launch_t(const AttnLaunch& L, hipStream_t stream) {
   dim3 grid((L.npad / 128) * L.heads * L.seqs), block(256);
-  if (L.dh == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 64>), grid, block, 0, stream, L);
-  else if (L.dh == 32) hipLaunchKernelGGL((attn_time2_kernel<T, 32>), grid, block, 0, stream, L);
+  if (L.dh == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 64, kKeysPerTile>), grid, block, 0, stream, L);
+  else if (L.dh == 32) hipLaunchKernelGGL((attn_time2_kernel<T, 32, kKeysPerTile>), grid, block, 0, stream, L);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
