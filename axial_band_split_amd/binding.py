@@ -316,6 +316,8 @@ class Core:
         torch = _torch()
         _check_dense(wave)
         S, L = wave.shape
+        if S != self.S:
+            raise ValueError(f"the core separates {self.S}-channel tracks, got {S} channels")
         ws = torch.empty(mbr_separate_workspace_size(self.handle, L, hop), dtype=torch.uint8, device=wave.device)
         out = torch.empty((self.cfg.num_stems, S, L), dtype=torch.float32, device=wave.device)
         mbr_separate(self.handle, wave.data_ptr(), L, hop, ws.data_ptr(), out.data_ptr(), _stream_ptr(stream))
