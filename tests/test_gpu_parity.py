@@ -332,3 +332,30 @@ def test_zero_dc_on_the_fp32_path():
     ref = M.forward(x, dataclasses.replace(ocfg(w), zero_dc=True), ws)
     assert np.all(y[:, :2] == 0.0)
     assert rel_l2(y, ref) <= TOL[synth.F32]
+
+
+def test_forward_replays_from_a_hip_graph():
+    """A forward captured in a HIP graph (it allocates nothing, clears nothing with memsets and never
+    waits on the host) replays bitwise like the eager call, three times with eager work between."""
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(frames=97, depth=1)
+    say("[graph] capture and replay, T=97")
+    cfg, ws = build(w)
+    core = binding.Core(cfg, ws)
+    x = torch.from_numpy(synth.draw_input(w)).cuda()
+    out = torch.empty(core.output_shape(1), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        core.forward(x, out, side)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        core.forward(x, out, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        (x * 2.0).sum().item()
+    core.close()
