@@ -217,11 +217,57 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
   char* vlds = vlds_all[wave];
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int DCH = DH / EPC;
-  f32x4 s[4][4];
+  const int I = L.heads * DH;
+  const int BT = L.batch * L.frames;
+  // Softmax over the keys, P.V and the gated store of the 16 queries of column block c, from their
+  // S^T tiles sc[r] (keys 16r .. 16r + 15).  One block at a time keeps 32 accumulator registers
+  // live instead of 128, which leaves room for more waves per SIMD.
+  auto column = [&](int c, f32x4 (&sc)[4]) {
+    float mx = kNegBig;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4; ++e) {
+        const int key = r * 16 + 4 * g4 + e;
+        const float v = key < n ? sc[r][e] * L.scale_log2 : kNegBig;
+        sc[r][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sc[r][e] - mx);
+        sc[r][e] = p;
+        sum += p;
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    f32x4 oacc[DH / 16];
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < PV; ++m) {
+      const typename PFrag<T>::type pf = PFrag<T>::make(sc[m * SPP], sc[m * SPP + SPP - 1]);
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d) mma(oacc[d], PFrag<T>::vload(vlds + (d * 16 + l16) * VROW, m, g4), pf);
+    }
+    const int q = c * 16 + l16;
+    if (q >= n) return;
+    const size_t row = (size_t)q * BT + seq;
+    const float scale = L.gates[row * L.heads + h] / sum;
+    T* dst = (T*)L.o + row * I + h * DH + 4 * g4;
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d) {
+      typename Vec4<T>::type o4;   // 4 consecutive dims: one 8-byte (16-byte for fp32) store
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = cvt<T>(oacc[d][e] * scale);
+      *(typename Vec4<T>::type*)(dst + d * 16) = o4;
+    }
+  };
   if constexpr (sizeof(T) == 2) {
     // Every load of the wave is issued before the first is used (one memory round trip): V four
     // keys x 8 dims per lane and pass, then the Q and K fragments of every K step.
@@ -255,12 +301,22 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
       }
     }
 #pragma unroll
-    for (int st = 0; st < DSTEPS; ++st)
+    for (int c = 0; c < 4; ++c) {
+      f32x4 sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) sc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) mma(s[r][c], kf[st][r], qf[st][c]);
+      for (int st = 0; st < DSTEPS; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mma(sc[r], kf[st][r], qf[st][c]);
+      column(c, sc);
+    }
   } else {
+    f32x4 s[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     // this wave's V [64 keys][DH] -> V^T [DH][keys] in its own LDS slice
     for (int c = lane; c < 64 * DCH; c += 64) {
       const int r = c / DCH, p = c - r * DCH;
@@ -281,67 +337,10 @@ __global__ __launch_bounds__(256) void attn_band_kernel(AttnLaunch L) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) mma(s[r][c], kf[r], qf[c]);
     }
-  }
-  float lsum[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float mx = kNegBig;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = r * 16 + 4 * g4 + e;
-        const float v = key < n ? s[r][c][e] * L.scale_log2 : kNegBig;
-        s[r][c][e] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[r][c][e] - mx);
-        s[r][c][e] = p;
-        sum += p;
-      }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    lsum[c] = sum;
-  }
-  f32x4 oacc[DH / 16][4];
-#pragma unroll
-  for (int d = 0; d < DH / 16; ++d)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) oacc[d][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < PV; ++m) {
-    typename PFrag<T>::type pf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pf[c] = PFrag<T>::make(s[m * SPP][c], s[m * SPP + SPP - 1][c]);
-#pragma unroll
-    for (int d = 0; d < DH / 16; ++d) {
-      const auto a = PFrag<T>::vload(vlds + (d * 16 + l16) * VROW, m, g4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) mma(oacc[d][c], a, pf[c]);
-    }
-  }
-  const int I = L.heads * DH;
-  const int BT = L.batch * L.frames;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int q = c * 16 + l16;
-    if (q >= n) continue;
-    const size_t row = (size_t)q * BT + seq;
-    const float scale = L.gates[row * L.heads + h] / lsum[c];
-    T* dst = (T*)L.o + row * I + h * DH + 4 * g4;
-#pragma unroll
-    for (int d = 0; d < DH / 16; ++d) {
-      typename Vec4<T>::type o4;   // 4 consecutive dims: one 8-byte (16-byte for fp32) store
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = cvt<T>(oacc[d][c][e] * scale);
-      *(typename Vec4<T>::type*)(dst + d * 16) = o4;
+    for (int c = 0; c < 4; ++c) {
+      f32x4 sc[4] = {s[0][c], s[1][c], s[2][c], s[3][c]};
+      column(c, sc);
     }
   }
 }
