@@ -122,9 +122,18 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
     voff[C::A_LD + j] = (int)(min(row, brows - 1) * ldb_b) + c * 16;
     dst[C::A_LD + j] = C::A_BYTES + (j * NW + w) * 1024;
   }
+  // K order rotated by the column tile: the tiles that share an A panel (same m0) run at the same
+  // time, and in plain order all of them would ask for each K chunk at once and every one would
+  // wait for the same HBM fill.  Rotated by one chunk per column tile, their prologues request the
+  // whole panel together and the later steps find their chunk already in L2.  (Only the column
+  // tile: a row's sum order must not depend on where the row sits in the batch.)
+  const int nk = g.K >> 5;
+  const int krot = nk > 1 ? (n0 / BN) % nk : 0;
   auto issue = [&](int ks) {
     char* base = smem + (ks % NS) * C::STAGE;
-    const int ko = ks * 64;
+    int kc = ks + krot;
+    if (kc >= nk) kc -= nk;
+    const int ko = kc * 64;
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) buffer_dma16(j < C::A_LD ? ars : brs, voff[j], ko, base + dst[j]);
   };
@@ -137,7 +146,6 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = g.K >> 5;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
@@ -296,8 +304,29 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
       int which = 0;
       if constexpr (EPI == EPI_QKV) which = cbase / (qa.heads * qa.dh);
       if (EPI == EPI_QKV && which == 2 && qa.axis == 0) {
-        // time axis: v goes out transposed, [seq][h][dh][npad]; lane%32 = row, so every store
-        // instruction writes 32 consecutive positions of one head dimension per half wave
+        // time axis: v goes out transposed, [seq][h][dh][npad]
+        const int seq0 = rbase / qa.frames, pos0 = rbase - seq0 * qa.frames;
+        if (rbase + 32 <= M && pos0 + 32 <= qa.frames && (pos0 & 3) == 0) {
+          // the 32 rows are positions pos0 .. pos0+31 of one sequence, pos0 a multiple of 4: lane
+          // (column 8k + lane/8, rows 4(lane%8) .. +3) writes 8 bytes, so 8 lanes fill 64 bytes of
+          // one V^T row and an instruction covers 8 of them
+          const int j = lane & 7;
+          float scr[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) scr[t] = __shfl(sc_mine, 4 * j + t, 64);
+          T* vt = (T*)qa.v + ((size_t)seq0 * qa.heads * qa.dh + (cbase - 2 * qa.heads * qa.dh)) * qa.npad + pos0 + 4 * j;
+#pragma unroll 4
+          for (int k = 0; k < 8; ++k) {
+            const int c = 8 * k + (lane >> 3);
+            typename Vec4<T>::type h4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) h4[t] = cvt<T>(ep[(4 * j + t) * ES + c] * scr[t]);
+            *(typename Vec4<T>::type*)(vt + (size_t)c * qa.npad) = h4;
+          }
+          continue;
+        }
+        // otherwise lane%32 = row: every store instruction writes 32 consecutive positions of one
+        // head dimension per half wave
         const int row = rbase + r32;
         if (row < M) {
           const float sc = sc_mine;

@@ -5,8 +5,8 @@
 
 A step is one forward of the whole core (band gather and embedding, every axial Transformer, the
 mask head, the mask average) over one batch of seeded synthetic spectra already resident in HBM.
-Prints one JSON line: core audio-seconds per second, the per-kernel device times measured with HIP
-events on the launch stream, the roofline of the dominant kernel, the fp64 CPU oracle timed on
+Prints one JSON line: core audio-seconds per second, the median / p10 / p90 of single forwards
+and the per-kernel device times (HIP events on the launch stream), the roofline of the dominant kernel, the fp64 CPU oracle timed on
 a bounded sample of the same workload, and (beside the headline figure) the separation of a
 synthetic 60 s stereo track through STFT, core, iSTFT and the chunked overlap-add.
 """
@@ -176,6 +176,19 @@ def main() -> int:
     value = w.audio_seconds * args.steps / (t1 - t0)
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, {value:.1f} audio-s/s")
 
+    # spread of single forwards: an event pair on the launch stream around each one (after the
+    # timed region, so the events cost it nothing)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        core.forward(x, out, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    spread = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "forwards": len(per)}
+    log(f"[bench] single forwards: median {spread['median']:.3f} ms, p10 {spread['p10']:.3f}, p90 {spread['p90']:.3f}")
+
     # per-kernel device time: HIP event pairs around every launch on the launch stream
     acc = {k: [0.0, 0] for k in binding.KERNEL_KINDS}
     tp0 = time.perf_counter()
@@ -243,6 +256,7 @@ def main() -> int:
         "attn_gemm": {"tflops": ga_tflops, "peak": peak_mfma, "frac": ga_tflops / peak_mfma,
                       "flops_per_step": fl["total"], "device_ms": ga_ms},
         "e2e_tflops": fl["total"] / (ms_step * 1e-3) / 1e12,
+        "forward_ms": spread,
         "device_ms_per_step": dev_ms,
         "profiled_ms_per_step": (tp1 - tp0) * 1e3 / P,
         "kernels": kernels,
