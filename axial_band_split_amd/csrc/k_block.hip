@@ -70,6 +70,14 @@ __device__ __forceinline__ void for_regions(Fn fn, std::integer_sequence<int, g.
   (fn(std::integral_constant<int, g + 1>{}), ...);
 }
 
+// fn(integral_constant<i>) for i = 0 .. N-1 (a loop whose index can select template arguments)
+template <typename Fn, int... i>
+__device__ __forceinline__ void static_for_impl(Fn fn, std::integer_sequence<int, i...>) {
+  (fn(std::integral_constant<int, i>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn fn) { static_for_impl(fn, std::make_integer_sequence<int, N>{}); }
+
 template <int N, int GS, int VPM, typename F, typename RD, typename MM, typename HK>
 __device__ __forceinline__ void pipelined(RD rd, MM mm, HK hook) {
   static_assert(N % GS == 0, "group size");
@@ -166,37 +174,78 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
 
-  // x (fp32) straight into the accumulators
+  // ---- x1 = x + o W_out^T; the attention output is read as B operands one stage ahead.  The
+  // accumulators start at zero and x (fp32, 4 DT 16-byte loads per lane) arrives in KO parts, part p
+  // requested after stage p-1's weights and added at the start of stage p+2 (the last two after
+  // the loop): every block of a device pass starts at once, and waiting for the whole residual
+  // before the first product would expose one chip-wide burst of reads per pass.
   f32x16 acc[DT];
-  const float* xr = L.X + tload * D + 4 * h;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = *(const float4*)(xr + 32 * t + 8 * j);
-      acc[t][4 * j + 0] = v.x;
-      acc[t][4 * j + 1] = v.y;
-      acc[t][4 * j + 2] = v.z;
-      acc[t][4 * j + 3] = v.w;
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  constexpr int XP = 4 * DT / KO;   // 16-byte residual loads per part
+  static_assert(XP * KO == 4 * DT, "residual parts");
+  const float* xr = L.X + tload * D + 4 * h;
+  float4 xs[3][XP];
+  // residual 16-byte piece e = 4t + j holds accumulator tile t, elements 4j .. 4j+3
+  // the wait counts below assume this issue order: keep the compiler from moving loads across
+  auto order = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_x = [&](auto p_) {
+    constexpr int p = decltype(p_)::value;
+    order();
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int e = p * XP + i;
+      xs[p % 3][i] = *(const float4*)(xr + 32 * (e >> 2) + 8 * (e & 3));
     }
-
-  // ---- x1 = x + o W_out^T; the attention output is read as B operands one stage ahead
+  };
+  auto add_x = [&](auto p_) {
+    constexpr int p = decltype(p_)::value;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int e = p * XP + i, t = e >> 2, j = e & 3;
+      acc[t][4 * j + 0] += xs[p % 3][i].x;
+      acc[t][4 * j + 1] += xs[p % 3][i].y;
+      acc[t][4 * j + 2] += xs[p % 3][i].z;
+      acc[t][4 * j + 3] += xs[p % 3][i].w;
+    }
+  };
   const T* orow = (const T*)L.O + tload * I + 8 * h;
   frag ob[2][4];
+  order();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ob[0][ks] = *(const frag*)(orow + 16 * ks);
-#pragma unroll
-  for (int st = 0; st < KO; ++st) {
-    stage_begin(st);
-    if (st + 1 < KO)
+  load_x(std::integral_constant<int, 0>{});
+  // loads issued after stage st's weights when stage st begins (in issue order: the weights of
+  // stage 1, o of stage 0 and residual part 0 for st = 0; those plus stage 0's o, weights and part
+  // for st = 1; then the part after the weights of st, and stage st-1's o, weights and part)
+  auto wait_outproj = [&](auto st_) {
+    constexpr int st = decltype(st_)::value;
+    constexpr int N = st == 0 ? R + 4 + XP : st == 1 ? R + 8 + 2 * XP : R + 4 + 2 * XP;
+    static_assert(N < 64, "vmcnt range");
+    wait_vm<N>();
+    block_barrier();
+  };
+  static_for<KO>([&](auto st_) {
+    constexpr int st = decltype(st_)::value;
+    wait_outproj(st_);
+    if constexpr (st + 1 < KO)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) ob[(st + 1) & 1][ks] = *(const frag*)(orow + 64 * (st + 1) + 16 * ks);
+    if constexpr (st >= 2) add_x(std::integral_constant<int, st - 2>{});
     const char* sl = smem + (st % NS) * SB + lane * 16;
     // fragment f = ks * DT + t
     pipelined<4 * DT, GS, 0, frag>([&](int f) { return *(const frag*)(sl + f * 1024); },
                                    [&](int f, const frag& a) { mma32(acc[f % DT], a, ob[st & 1][f / DT]); }, none);
     stage_end(st);
-  }
+    if constexpr (st + 1 < KO) load_x(std::integral_constant<int, st + 1>{});
+  });
+  add_x(std::integral_constant<int, KO - 2>{});
+  add_x(std::integral_constant<int, KO - 1>{});
 
   // ---- RMSNorm_f(x1) as B operands (the gain is in W_1)
   float ss = 0.f;

@@ -359,3 +359,22 @@ def test_forward_replays_from_a_hip_graph():
         assert torch.equal(out, ref), f"replay {i}"
         (x * 2.0).sum().item()
     core.close()
+
+
+def test_forward_refuses_a_batch_outside_one_to_max_batch():
+    """Batch 0 and max_batch + 1 are argument errors (MBR_E_ARG) that launch nothing; the call with
+    a valid batch on the same buffers still succeeds afterwards."""
+    w = synth.WORKLOADS["tiny_fp32"]
+    cfg, ws = build(w, max_batch=2)
+    core = binding.Core(cfg, ws)
+    x = torch.from_numpy(synth.draw_input(w, batch=3)).cuda()
+    out = torch.empty(core.output_shape(3), dtype=torch.float32, device="cuda")
+    for batch in (0, 3):
+        say(f"[batch] {batch} with max_batch 2")
+        with pytest.raises(binding.MbrError) as e:
+            binding.mbr_core_forward(core.handle, x.data_ptr(), out.data_ptr(), batch, 0)
+        assert e.value.code == -1 and "batch" in binding.mbr_last_error()
+    binding.mbr_core_forward(core.handle, x.data_ptr(), out.data_ptr(), 2, 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:2]).all()
+    core.close()

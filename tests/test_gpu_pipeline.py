@@ -126,3 +126,35 @@ def test_separation_half_precision_vocals_core_matches_oracle():
     err = rel_l2(got, want)
     say(f"[separate] rel L2 = {err:.2e}")
     assert got.shape == want.shape and err < 2e-2
+
+
+@pytest.mark.parametrize("L", [2, 100, 1500])
+def test_separation_of_tracks_shorter_than_a_chunk(L):
+    """Tracks of 2 samples (the shortest accepted), 100 (under two borders: no reflect padding, one
+    zero-padded chunk) and 1500 (reflect-padded to 1910: one chunk with a reflected tail, then 67
+    samples in a zero-padded one) through the tiny fp32 core (2048-sample chunks, hop 64), against
+    the oracle's separation."""
+    w = synth.WORKLOADS["tiny_fp32"].replace(frames=33, batch=2)
+    cfg = binding.config(w)
+    ws = synth.draw_weights(binding.inventory(cfg), w.dtype, seed=0, std=0.1)
+    oc = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads, w.dim_head,
+                      w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+    x = np.random.default_rng(5).standard_normal((2, L)).astype(np.float32)
+    say(f"[separate] tiny core, short track L={L}")
+    core = binding.Core(cfg, ws)
+    got = core.separate(torch.from_numpy(x).cuda(), 64).cpu().numpy()
+    core.close()
+    want = P.separate(x.astype(np.float64), lambda spec: M.forward(spec, oc, ws), 256, 64, 2048, 1)
+    err = rel_l2(got, want)
+    say(f"[separate] rel L2 = {err:.2e}")
+    assert got.shape == want.shape == (1, 2, L) and err < 1e-4
+
+
+def test_separation_refuses_a_one_sample_track():
+    w = synth.WORKLOADS["tiny_fp32"].replace(frames=33, batch=1)
+    cfg = binding.config(w)
+    core = binding.Core(cfg, synth.draw_weights(binding.inventory(cfg), w.dtype, seed=0))
+    x = torch.zeros((2, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.MbrError):
+        core.separate(x, 64)
+    core.close()
