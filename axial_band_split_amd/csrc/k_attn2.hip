@@ -123,6 +123,8 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     for (int j = 0; j < VLD; ++j) buffer_dma16(vrs, vsrc[j], kt * KT * 2, st + vdst[j]);
   };
 
+  // the lane's gate, requested first (read at the end it would wait a memory round trip there)
+  const float gate = q0 + l32 < n ? L.gates[((size_t)seq * L.frames + q0 + l32) * L.heads + h] : 0.f;
   // q fragments: B operand of S^T = K Q^T; lane holds query q0 + l32, dims 16*ks + 8*g .. +7
   frag qf[KSTEPS];
 #pragma unroll
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   const int q = q0 + l32;
   if (q >= n) return;
   const size_t row = (size_t)seq * L.frames + q;
-  const float scale = L.gates[row * L.heads + h] / lsum;
+  const float scale = gate / lsum;
   T* dst = (T*)L.o + row * (L.heads * DH) + h * DH;
 #pragma unroll
   for (int d = 0; d < DT; ++d)
