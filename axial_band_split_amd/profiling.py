@@ -102,12 +102,21 @@ def counters_md(csv_path: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def source_hash() -> str:
+# the sources a kernel class is built and launched from: a counter record stays valid while these
+# are unchanged (changes to other kernels do not touch it)
+KIND_SOURCES = {
+    "block": ("k_block.hip", "kcommon.h", "kernels.h", "mbr_core.cpp"),
+}
+
+
+def source_hash(files=None) -> str:
+    """Hash of the named files under csrc/ (all kernel sources when None)."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    names = sorted(files) if files else sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    for f in names:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -124,7 +133,7 @@ def _one(csv_path: str, counter: str, regex: str) -> float:
     return sum(sum(v) / len(v) for v in per.values())
 
 
-def traffic_record(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, regex, command) -> dict:
+def traffic_record(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, regex, command, sources=None) -> dict:
     copy = r"copyBuffer|elementwise_kernel.*(copy|Copy)|direct_copy"
     fetch_kib = _one(fetch_csv, "FETCH_SIZE", regex)
     write_kib = _one(write_csv, "WRITE_SIZE", regex)
@@ -137,7 +146,8 @@ def traffic_record(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, regex, co
             "fetch_factor": ff, "write_factor": wf,
             "bytes_per_launch": fetch_kib * 1024 * ff + write_kib * 1024 * wf,
             "calibration": f"device copy of {CAL_BYTES} bytes: FETCH_SIZE {cal_fetch:.0f} KiB, WRITE_SIZE {cal_write:.0f} KiB",
-            "source_sha": source_hash(), "command": command}
+            "source_files": list(sources) if sources else None, "source_sha": source_hash(sources),
+            "command": command}
 
 
 N_SIMD, N_XCD = 1024, 8      # MI355X: 256 compute units x 4 SIMDs, 8 XCDs
@@ -260,7 +270,10 @@ def main(argv=None):
     elif args.what == "counters":
         open(args.out, "w").write(counters_md(args.csv, args.command))
     else:
-        rec = traffic_record(args.fetch, args.write, args.cal_fetch, args.cal_write, args.regex, args.command)
+        from axial_band_split_amd import roofline as R
+        kind = next((k for k, v in R.KIND_REGEX.items() if v == args.regex), None)
+        rec = traffic_record(args.fetch, args.write, args.cal_fetch, args.cal_write, args.regex, args.command,
+                             KIND_SOURCES.get(kind))
         json.dump(rec, open(args.out, "w"), indent=1)
     return 0
 

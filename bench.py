@@ -44,7 +44,7 @@ def traffic_for(workload: str, kind: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_regex") != KIND_REGEX.get(kind) or rec.get("source_sha") != profiling.source_hash():
+    if rec.get("kernel_regex") != KIND_REGEX.get(kind) or rec.get("source_sha") != profiling.source_hash(rec.get("source_files")):
         return None
     return rec["bytes_per_launch"]
 
