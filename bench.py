@@ -87,11 +87,16 @@ def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
     except Exception:
         pass
     cores = max(threads or 1, M._WORKERS)
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        blas = None
     return {"value": w.audio_seconds / est, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
             "sample": (f"fp64 numpy oracle on {w.name}: band embedding, {layers} of {w.depth} layers (time + band "
                        f"Transformer), mask head and average of stem 0, each timed once ({t3 - t0:.1f} s); "
                        f"forward estimated as embed + {w.depth} x mean layer + {w.num_stems} x mask head = {est:.1f} s"),
-            "host_cpus": os.cpu_count(), "blas_threads": threads, "seconds_sampled": t3 - t0}
+            "host_cpus": os.cpu_count(), "blas": blas, "blas_threads": threads, "seconds_sampled": t3 - t0}
 
 
 def separation(w: synth.Workload, ws, seconds: float, repeats: int) -> dict:
