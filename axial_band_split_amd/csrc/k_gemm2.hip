@@ -14,10 +14,12 @@
 //     tiles are consecutive) so that each XCD (workgroups are dealt round-robin to the 8 XCDs)
 //     receives one contiguous run of tiles: neighbouring tiles share operand panels in that XCD's
 //     L2;
+//   * each tile walks K starting at chunk (column tile mod K/32), so the tiles reading one A panel
+//     at the same time ask for different chunks and the later ones hit L2;
 //   * the epilogue stages 32 accumulator rows of a wave at a time through LDS and writes 16-byte
 //     vectors: rows of q, k, v (rotary applied to the pairs a lane already holds; the time axis'
-//     v transposed), GELU / tanh outputs, fp32 residual updates, and the GLU of paired 32-feature
-//     value / gate blocks stored feature-major.
+//     v transposed, 8 bytes of 4 positions per lane), GELU / tanh outputs, fp32 residual updates,
+//     and the GLU of paired 32-feature value / gate blocks stored feature-major.
 #include "kcommon.h"
 #include "kernels.h"
 
