@@ -261,6 +261,83 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch L) {
     for (int c = lane; c < kp2; c += 64) dst[(size_t)r * kp2 + c] = tile[r * rs + c];
 }
 
+// The same gather for bands of up to 16 * MAXJ pairs, with more workgroups and one read of the
+// input: 16 frames of one band per workgroup; lane l of wave w takes frame t0 + l % 16 and the
+// band's pairs g, g + 16, ... (g = 4w + l / 16), holds them in registers while the band norm is
+// summed (through LDS) and writes them normalised into an LDS tile (rows of kpad/2 + 1 units) that
+// goes out as the band's 16 contiguous rows of U.  For one pair, 16 frames are 128 contiguous bytes
+// of the input.
+template <typename T, int LAYOUT, int MAXJ>
+__global__ __launch_bounds__(256) void gather16_kernel(GatherLaunch L) {
+  typedef typename PairUnit<T>::type P;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  P* tile = (P*)lds_raw;                       // [16][kpad/2 + 1]
+  __shared__ float part[16][17];               // [pair group][frame]
+  __shared__ float scale[16];
+  const int band = blockIdx.z, b = blockIdx.y;
+  const int t0 = blockIdx.x * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int fr = lane & 15, g = 4 * w + (lane >> 4);
+  const int T_ = L.frames;
+  const int t = t0 + fr;
+  const int tl = t < T_ ? t : T_ - 1;          // frames past the end read the last one, never stored
+  const int foff = L.band_info[band * 4 + 0], width = L.band_info[band * 4 + 1];
+  const int kpad = L.band_info[band * 4 + 2], ucol = L.band_info[band * 4 + 3];
+  const int npairs = width / 2, kp2 = kpad / 2, rs = kp2 + 1;
+  const int F = L.n_freqs, S = L.channels, FS = F * S;
+  const int32_t* pidx = L.gather_pair + foff / 2;
+  int pj[MAXJ];
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u) {
+    const int j = g + 16 * u;
+    pj[u] = pidx[j < npairs ? j : 0];
+  }
+  float re[MAXJ], im[MAXJ];
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u) {
+    if constexpr (LAYOUT == 0) {
+      const float2 z = *(const float2*)(L.in + (((size_t)b * FS + pj[u]) * T_ + tl) * 2);
+      re[u] = z.x;
+      im[u] = z.y;
+    } else {
+      const int f = pj[u] / S, s = pj[u] - f * S;
+      const float* base = L.in + ((size_t)b * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + tl;
+      re[u] = base[0];
+      im[u] = base[(size_t)F * T_];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u)
+    if (g + 16 * u < npairs) ss += re[u] * re[u] + im[u] * im[u];
+  part[g][fr] = ss;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) tot += part[q][threadIdx.x];
+    scale[threadIdx.x] = 1.0f / fmaxf(sqrtf(tot), kNormEps);
+  }
+  __syncthreads();
+  const float sc = scale[fr];
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u) {
+    const int j = g + 16 * u;
+    if (j < npairs) tile[fr * rs + j] = PairUnit<T>::make(re[u] * sc, im[u] * sc);
+  }
+  for (int i = threadIdx.x; i < 16 * (kp2 - npairs); i += 256) {
+    const int r = i / (kp2 - npairs), j = npairs + i - r * (kp2 - npairs);
+    tile[r * rs + j] = PairUnit<T>::make(0.f, 0.f);
+  }
+  __syncthreads();
+  // rows b*T + t0 .. of band `band`: contiguous in U at column block ucol, kpad/2 units a row
+  const int rows = min(16, T_ - t0);
+  const size_t BT = (size_t)L.batch * T_;
+  P* dst = (P*)((T*)L.U + (size_t)ucol * BT + ((size_t)b * T_ + t0) * kpad);
+  for (int r = w; r < rows; r += 4)
+    for (int c = lane; c < kp2; c += 64) dst[(size_t)r * kp2 + c] = tile[r * rs + c];
+}
+
 // ---------------------------------------------------------------------------------- average
 // [P1] "The forward chain": the band masks go back to their (bin, channel) pairs and each value
 // is divided by the number of bands covering its bin.  Instead of a scatter with atomics, every
@@ -317,8 +394,23 @@ hipError_t launch_norm(const NormLaunch& L, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+template <typename T, int LAYOUT, int MAXJ>
+hipError_t gather16_t(const GatherLaunch& L, hipStream_t stream) {
+  dim3 grid((L.frames + 15) / 16, L.batch, L.num_bands), block(256);
+  const size_t lds = (size_t)16 * (L.max_kpad / 2 + 1) * 2 * sizeof(T);
+  hipError_t e = hipFuncSetAttribute((const void*)gather16_kernel<T, LAYOUT, MAXJ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gather16_kernel<T, LAYOUT, MAXJ>), grid, block, lds, stream, L);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t gather_t(const GatherLaunch& L, hipStream_t stream) {
+  // bands of up to 384 pairs: 16 frames per workgroup, pairs held in registers
+  const int maxp = L.max_kpad / 2;
+  if (maxp <= 16 * 8) return L.layout == 0 ? gather16_t<T, 0, 8>(L, stream) : gather16_t<T, 1, 8>(L, stream);
+  if (maxp <= 16 * 24) return L.layout == 0 ? gather16_t<T, 0, 24>(L, stream) : gather16_t<T, 1, 24>(L, stream);
   dim3 grid((L.frames + 63) / 64, L.batch, L.num_bands), block(256);
   const size_t lds = (size_t)64 * (L.max_kpad / 2 + 1) * 2 * sizeof(T) + (size_t)(L.max_kpad / 2) * 4;
   if (lds > 160 * 1024 - 2048) return hipErrorInvalidValue;
