@@ -270,6 +270,7 @@ def main(argv=None):
     elif args.what == "counters":
         open(args.out, "w").write(counters_md(args.csv, args.command))
     else:
+        sys.path.insert(0, os.path.dirname(HERE))
         from axial_band_split_amd import roofline as R
         kind = next((k for k, v in R.KIND_REGEX.items() if v == args.regex), None)
         rec = traffic_record(args.fetch, args.write, args.cal_fetch, args.cal_write, args.regex, args.command,
