@@ -2,6 +2,7 @@
 // sequence of one forward.  The functions declared in include/mbr_core.h live here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -216,6 +217,19 @@ int setup_tables_and_groups(mbr_core* c) {
     add_tiles((int)groups.size() - 1, g.N, c->v_embed);
   }
   c->n_embed = (int)tiles.size();
+  {
+    // the embedding's K differs per band (32 .. 544 at the vocals shape): longest K first, dealt so
+    // that each XCD's contiguous run of the table (the kernel gives each XCD one run, in order)
+    // holds every 8th tile of that order
+    std::vector<GemmTile> t(tiles.begin() + c->t_embed, tiles.begin() + c->n_embed);
+    std::stable_sort(t.begin(), t.end(),
+                     [&](const GemmTile& a, const GemmTile& b) { return groups[a.group].K > groups[b.group].K; });
+    const int nb = (int)t.size(), per = nb >> 3, rem = nb & 7;
+    for (int i = 0; i < nb; ++i) {
+      const int x = i & 7, slot = i >> 3;
+      tiles[c->t_embed + x * per + std::min(x, rem) + slot] = t[i];
+    }
+  }
   const int nl = cfg.mask_depth + 1;
   c->g_mask.assign(cfg.num_stems, std::vector<int>(nl));
   c->t_mask.assign(cfg.num_stems, std::vector<int>(nl));
