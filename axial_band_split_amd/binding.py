@@ -227,6 +227,7 @@ def istft_masked(spec, masks, channels: int, length: int, n_fft: int, hop: int, 
     out = torch.empty((stems, channels, length), dtype=torch.float32, device=spec.device)
     mbr_istft_masked(spec.data_ptr(), masks.data_ptr(), stems, channels, length, n_fft, hop, ws.data_ptr(),
                      out.data_ptr(), _stream_ptr(stream))
+    _keep_for_stream(ws, stream)
     return out
 
 
@@ -264,6 +265,18 @@ def _stream_ptr(stream) -> int:
     if stream is None:
         return _torch().cuda.current_stream().cuda_stream
     return int(getattr(stream, "cuda_stream", stream))
+
+
+def _keep_for_stream(buf, stream) -> None:
+    """A workspace allocated here (on torch's current stream) but used by work enqueued on
+    `stream`: tell torch's caching allocator that `stream` uses it, so the block is not handed to
+    another tensor before that stream has passed the work."""
+    if stream is None:
+        return
+    torch = _torch()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream != torch.cuda.current_stream().cuda_stream:
+        buf.record_stream(s)
 
 
 class Core:
@@ -321,6 +334,7 @@ class Core:
         ws = torch.empty(mbr_separate_workspace_size(self.handle, L, hop), dtype=torch.uint8, device=wave.device)
         out = torch.empty((self.cfg.num_stems, S, L), dtype=torch.float32, device=wave.device)
         mbr_separate(self.handle, wave.data_ptr(), L, hop, ws.data_ptr(), out.data_ptr(), _stream_ptr(stream))
+        _keep_for_stream(ws, stream)
         return out
 
     def profile(self, x, out, stream=None):

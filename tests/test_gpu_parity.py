@@ -31,6 +31,26 @@ def say(*a):
     print(*a, flush=True)
 
 
+def check_parts(tag, y, ref, w: synth.Workload, tol, frame_block=128):
+    """Relative L2 of every band's bins (all frames) and of every block of `frame_block` frames
+    (all bins), each at the bar `tol`, so that a defect confined to one band or to the ragged last
+    frames cannot hide in the global figure; prints the worst of each and the largest absolute
+    error relative to the largest reference value.  y, ref: one stem's masks in the io layout."""
+    S = w.audio_channels
+    a = M.read_input(np.asarray(y, np.float64), S, w.io_layout)      # [B, F*S, T, 2]
+    b = M.read_input(np.asarray(ref, np.float64), S, w.io_layout)
+    tables = ocfg(w).tables()
+    band = [rel_l2(a[:, p], b[:, p]) for p in tables.pairs]
+    T = a.shape[2]
+    blocks = [rel_l2(a[:, :, t:t + frame_block], b[:, :, t:t + frame_block]) for t in range(0, T, frame_block)]
+    mar = float(np.abs(a - b).max() / np.abs(b).max())
+    ib, it = int(np.argmax(band)), int(np.argmax(blocks))
+    say(f"[{tag}] worst band {ib}: {band[ib]:.2e}; worst {frame_block}-frame block {it}: {blocks[it]:.2e}; "
+        f"max abs err / max |ref| = {mar:.2e}")
+    assert max(band) <= tol, f"band {ib}: rel L2 {band[ib]:.3e}"
+    assert max(blocks) <= tol, f"frame block {it}: rel L2 {blocks[it]:.3e}"
+
+
 def build(w: synth.Workload, max_batch=None, std=0.02, gamma_std=0.02):
     cfg = binding.config(w, max_batch=max_batch)
     ws = synth.draw_weights(binding.inventory(cfg), w.dtype, seed=w.weight_seed, std=std, gamma_std=gamma_std)
@@ -58,6 +78,7 @@ def test_masks_match_oracle_full_size(name):
     say(f"[parity] {name}: rel L2 = {err:.3e} (tolerance {TOL[w.dtype]:.0e})")
     assert np.isfinite(y).all()
     assert err <= TOL[w.dtype]
+    check_parts(name, y, ref, w, TOL[w.dtype])
 
 
 def test_heavy_architecture_matches_oracle_at_short_length():
@@ -179,6 +200,77 @@ def test_silent_frames_and_a_silent_band_stay_finite():
         assert rel_l2(y, M.forward(x, ocfg(w), ws)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_silent_input_on_the_fused_block_path(dtype):
+    """The vocals architecture in 16 bits (dim 384: the fused post-attention kernel and its norms)
+    with a fifth of the frames zeroed and one band's bins zeroed: finite, and parity holds."""
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(frames=97, depth=2, dtype=dtype)
+    say(f"[edge] silent frames / band on the fused path, {synth.DTYPE_NAMES[dtype]}, T={w.frames}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    x[:, :, ::5, :] = 0.0
+    t = ocfg(w).tables()
+    x[:, t.pairs[7], :, :] = 0.0
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    assert np.isfinite(y).all()
+    ref = M.forward(x, ocfg(w), ws)
+    err = rel_l2(y, ref)
+    say(f"[edge] rel L2 = {err:.3e}")
+    assert err <= TOL[dtype]
+    check_parts("edge", y, ref, w, TOL[dtype], frame_block=32)
+
+
+def _score_jumps(x, w: synth.Workload, ws, key_tile=64):
+    """Oracle side: for the first time Transformer, the scores of every (band, head, query) in
+    log2 units (scale dh^-1/2 times log2 e), and how far the largest score over the keys after the
+    first tile of `key_tile` keys exceeds the largest over that first tile."""
+    c = ocfg(w)
+    wd = M.named(c, ws)
+    emb = M.band_embed(M.read_input(x, w.audio_channels, w.io_layout), c, wd, c.tables())
+    p, I, H, dh, T = "layer0.time.", c.inner, c.heads, c.dim_head, w.frames
+    ang = M.rope_angles(T, dh)
+    worst, rows = -np.inf, 0
+    for band in range(c.num_bands):
+        xn = M.rmsnorm(emb[0, :, band, :], wd[p + "attn.norm.gamma"])
+        qkv = xn @ wd[p + "attn.to_qkv.weight"].T
+        q = M.rope(qkv[:, :I].reshape(T, H, dh).transpose(1, 0, 2), ang)
+        k = M.rope(qkv[:, I:2 * I].reshape(T, H, dh).transpose(1, 0, 2), ang)
+        s = q @ k.transpose(0, 2, 1) * (dh ** -0.5) * np.log2(np.e)
+        jump = s[:, :, key_tile:].max(-1) - s[:, :, :key_tile].max(-1)
+        worst = max(worst, float(jump.max()))
+        rows += int((jump > 8.0).sum())
+    return worst, rows
+
+
+@pytest.mark.parametrize("dtype,frames", [(synth.F16, 97), (synth.BF16, 256), (synth.F16, 1100)])
+def test_time_attention_reference_moves_with_peaked_scores(dtype, frames):
+    """Peaked attention, as trained weights give it: the first time Transformer's attention gain
+    times 6 (scores times 36), so that for some queries a later key tile's largest score exceeds
+    the first tile's by more than 8 (log2 units, checked on the oracle side).  The 16-bit time
+    attention then raises its exponentials' reference and rescales what it has accumulated; the
+    masks must still match the oracle."""
+    w = synth.WORKLOADS["chunk11s_fp16"].replace(frames=frames, depth=1, dtype=dtype)
+    say(f"[rescale] {synth.DTYPE_NAMES[dtype]} T={frames}")
+    cfg, ws = build(w)
+    names = [n for n, _, _ in M.inventory(ocfg(w))]
+    gi = names.index("layer0.time.attn.norm.gamma")
+    ws[gi] = synth.round_to_dtype(ws[gi] * 6.0, dtype)
+    x = synth.draw_input(w)
+    worst, rows = _score_jumps(x, w, ws)
+    say(f"[rescale] largest jump of a later key tile over the first: {worst:.1f} (log2); rows over 8: {rows}")
+    assert worst > 8.0 and rows > 0
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, ocfg(w), ws)
+    err = rel_l2(y, ref)
+    say(f"[rescale] rel L2 = {err:.3e}")
+    assert np.isfinite(y).all() and err <= TOL[dtype]
+    check_parts("rescale", y, ref, w, TOL[dtype], frame_block=64 if frames < 256 else 128)
+
+
 def test_forward_is_deterministic():
     w = synth.WORKLOADS["t256_fp16"]
     say("[det] t256 twice")
@@ -192,20 +284,31 @@ def test_forward_is_deterministic():
     assert torch.equal(a, b)
 
 
-def test_heavy_full_size_batch_consistency():
-    """The heavy configuration at full size (4 chunks of 1100 frames): finite, and each chunk's
-    masks are bitwise those of a batch-1 call on that chunk (chunks never interact)."""
+@pytest.mark.timeout(1200)
+def test_heavy_full_size_against_oracle():
+    """The heavy configuration at full size (4 chunks of 1100 frames, dim 512, depth 12, bf16, the
+    launch configuration the benchmark times): finite; chunk 2 of the batch-4 call against the
+    oracle's forward of that chunk (globally, per band and per 128-frame block, at the bf16 bar);
+    and each chunk's masks bitwise those of a batch-1 call on it (chunks never interact)."""
     w = synth.WORKLOADS["heavy_b4_d512_bf16"]
-    say("[heavy] full size, batch 4 vs batch 1")
+    say("[heavy] full size, batch 4: chunk 2 against the oracle and a batch-1 call")
     cfg, ws = build(w)
     core = binding.Core(cfg, ws)
-    xd = torch.from_numpy(synth.draw_input(w)).cuda()
+    x = synth.draw_input(w)
+    xd = torch.from_numpy(x).cuda()
     y4 = core.forward(xd)
     y1 = core.forward(xd[2:3].contiguous())
     torch.cuda.synchronize()
     assert torch.isfinite(y4).all()
     assert torch.equal(y4[2:3], y1)
+    y = y4[2:3].cpu().numpy()
     core.close()
+    say("[heavy] oracle forward of chunk 2 (fp64 on the host)")
+    ref = M.forward(x[2:3], ocfg(w), ws)
+    err = rel_l2(y, ref)
+    say(f"[heavy] chunk 2: rel L2 vs oracle = {err:.3e}")
+    assert err <= TOL[w.dtype]
+    check_parts("heavy", y, ref, w, TOL[w.dtype])
 
 
 @pytest.mark.parametrize("name,dtype,frames,depth", [("tiny_fp32", synth.F32, 32, 1), ("t256_fp16", synth.F16, 48, 1)])
@@ -410,4 +513,5 @@ def test_large_batches_and_long_chunks(frames, batch, picks, oracle_pick):
         err = rel_l2(yb[i:i + 1].cpu().numpy(), ref)
         say(f"[large] chunk {i}: rel L2 vs oracle = {err:.2e}")
         assert err <= TOL[w.dtype]
+        check_parts("large", yb[i:i + 1].cpu().numpy(), ref, w, TOL[w.dtype])
     core.close()

@@ -82,3 +82,44 @@ def test_chunk_tails_cover_both_padding_modes():
     tail; 2500: a reflected one)."""
     assert {m for _, _, m in P.chunk_plan(7000, 2048)[2]} == {"full", "reflect", "zero"}
     assert {m for _, _, m in P.chunk_plan(2500, 2048)[2]} == {"full", "reflect"}
+
+
+def test_core_input_layout_element_by_element():
+    """stft_repr [1, F*S, T, 2] holds channel s of bin f at pair f*S + s, real part first ([P1] "The
+    forward chain": the stereo channels merged into the frequency axis, bin-major)."""
+    rng = np.random.default_rng(3)
+    S, F, T = 2, 5, 4
+    z = rng.standard_normal((S, F, T)) + 1j * rng.standard_normal((S, F, T))
+    x = P.to_core_input(z)
+    assert x.shape == (1, F * S, T, 2)
+    for s in range(S):
+        for f in range(F):
+            for t in range(T):
+                assert x[0, f * S + s, t, 0] == z[s, f, t].real
+                assert x[0, f * S + s, t, 1] == z[s, f, t].imag
+
+
+def test_mask_product_with_non_unit_masks():
+    """Masks in the core's layout multiply the STFT as complex numbers, each channel by its own
+    pair: real constants a (left) and b (right) give a z_L and b z_R, a different pair per stem;
+    0 + 1i applied twice gives -z; one element checked against the complex product written out."""
+    rng = np.random.default_rng(4)
+    S, F, T = 2, 6, 3
+    z = rng.standard_normal((S, F, T)) + 1j * rng.standard_normal((S, F, T))
+    m = np.zeros((2, F * S, T, 2))
+    m[0, 0::2, :, 0], m[0, 1::2, :, 0] = 0.25, -3.0        # stem 0: a = 0.25 on the left, b = -3 on the right
+    m[1, 0::2, :, 0], m[1, 1::2, :, 0] = 2.0, 0.5          # stem 1: a = 2, b = 0.5
+    y = P.apply_masks(z, m)
+    assert y.shape == (2, S, F, T)
+    assert np.array_equal(y[0, 0], 0.25 * z[0]) and np.array_equal(y[0, 1], -3.0 * z[1])
+    assert np.array_equal(y[1, 0], 2.0 * z[0]) and np.array_equal(y[1, 1], 0.5 * z[1])
+    i = np.zeros((1, F * S, T, 2))
+    i[..., 1] = 1.0
+    twice = P.apply_masks(P.apply_masks(z, i)[0], i)[0]
+    assert np.allclose(twice, -z, rtol=0, atol=1e-15)
+    g = rng.standard_normal((1, F * S, T, 2))
+    y = P.apply_masks(z, g)
+    s, f, t = 1, 4, 2
+    mr, mi = g[0, f * S + s, t]
+    zr, zi = z[s, f, t].real, z[s, f, t].imag
+    assert y[0, s, f, t] == complex(zr * mr - zi * mi, zr * mi + zi * mr)
