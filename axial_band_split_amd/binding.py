@@ -37,12 +37,17 @@ _SIGS = {
                              C.c_int, C.c_int, C.c_void_p]),
     "mbr_k_gemm_variants": (C.c_int, []),
     "mbr_k_gelu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]),
+    "mbr_attention": (C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, C.c_void_p]),
     "mbr_stft": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
     "mbr_istft_workspace_size": (C.c_int64, [C.c_int, C.c_int, C.c_int, C.c_int]),
     "mbr_istft_masked": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_void_p,
                                    C.c_void_p, C.c_void_p]),
     "mbr_separate_workspace_size": (C.c_int64, [C.c_void_p, C.c_int64, C.c_int]),
     "mbr_separate": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "mbr_separate_workspace_size_strided": (C.c_int64, [C.c_void_p, C.c_int64, C.c_int, C.c_int64]),
+    "mbr_separate_strided": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
+                                       C.c_void_p]),
 }
 KERNEL_KINDS = ("gather", "embed", "norm", "qkv", "attn_time", "attn_band", "out_proj", "ffn1", "ffn2",
                 "mask_hidden", "mask_glu", "average", "block")
@@ -184,6 +189,13 @@ def mbr_k_gelu(x_ptr: int, y_ptr: int, n: int, stream_ptr: int = 0) -> None:
     _check(lib().mbr_k_gelu(C.c_void_p(x_ptr), C.c_void_p(y_ptr), n, C.c_void_p(stream_ptr)))
 
 
+def mbr_attention(dtype: int, q_ptr: int, k_ptr: int, vt_ptr: int, gates_ptr: int, o_ptr: int, seqs: int, heads: int,
+                  n: int, npad: int, dqk: int, dv: int, scale: float, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_attention(dtype, C.c_void_p(q_ptr), C.c_void_p(k_ptr), C.c_void_p(vt_ptr),
+                               C.c_void_p(gates_ptr or None), C.c_void_p(o_ptr), seqs, heads, n, npad, dqk, dv,
+                               scale, C.c_void_p(stream_ptr)))
+
+
 def mbr_stft(wave_ptr: int, channels: int, length: int, n_fft: int, hop: int, spec_ptr: int, stream_ptr: int = 0) -> None:
     _check(lib().mbr_stft(C.c_void_p(wave_ptr), channels, length, n_fft, hop, C.c_void_p(spec_ptr), C.c_void_p(stream_ptr)))
 
@@ -205,6 +217,16 @@ def mbr_separate_workspace_size(h, length: int, hop: int) -> int:
 def mbr_separate(h, wave_ptr: int, length: int, hop: int, ws_ptr: int, out_ptr: int, stream_ptr: int = 0) -> None:
     _check(lib().mbr_separate(h, C.c_void_p(wave_ptr), length, hop, C.c_void_p(ws_ptr), C.c_void_p(out_ptr),
                               C.c_void_p(stream_ptr)))
+
+
+def mbr_separate_workspace_size_strided(h, length: int, hop: int, stride: int) -> int:
+    return _check(lib().mbr_separate_workspace_size_strided(h, length, hop, stride))
+
+
+def mbr_separate_strided(h, wave_ptr: int, length: int, hop: int, stride: int, ws_ptr: int, out_ptr: int,
+                         stream_ptr: int = 0) -> None:
+    _check(lib().mbr_separate_strided(h, C.c_void_p(wave_ptr), length, hop, stride, C.c_void_p(ws_ptr),
+                                      C.c_void_p(out_ptr), C.c_void_p(stream_ptr)))
 
 
 def stft(wave, n_fft: int, hop: int, stream=None):
@@ -324,16 +346,19 @@ class Core:
         mbr_core_forward_debug(self.handle, x.data_ptr(), batch, stage, out.data_ptr(), _stream_ptr(stream))
         return out
 
-    def separate(self, wave, hop: int, stream=None):
-        """wave: float32 CUDA tensor [channels, length] -> stems [num_stems, channels, length]."""
+    def separate(self, wave, hop: int, stream=None, stride: int = 0):
+        """wave: float32 CUDA tensor [channels, length] -> stems [num_stems, channels, length].
+        stride: chunk stride in samples (0: 0.9 chunk)."""
         torch = _torch()
         _check_dense(wave)
         S, L = wave.shape
         if S != self.S:
             raise ValueError(f"the core separates {self.S}-channel tracks, got {S} channels")
-        ws = torch.empty(mbr_separate_workspace_size(self.handle, L, hop), dtype=torch.uint8, device=wave.device)
+        ws = torch.empty(mbr_separate_workspace_size_strided(self.handle, L, hop, stride), dtype=torch.uint8,
+                         device=wave.device)
         out = torch.empty((self.cfg.num_stems, S, L), dtype=torch.float32, device=wave.device)
-        mbr_separate(self.handle, wave.data_ptr(), L, hop, ws.data_ptr(), out.data_ptr(), _stream_ptr(stream))
+        mbr_separate_strided(self.handle, wave.data_ptr(), L, hop, stride, ws.data_ptr(), out.data_ptr(),
+                             _stream_ptr(stream))
         _keep_for_stream(ws, stream)
         return out
 

@@ -23,7 +23,11 @@
 //   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by (row >> 1) & 7, so the rows one
 //     fragment read touches spread over all LDS banks;
 //   * only the last key tile is masked (keys >= n), and the workgroup order keeps all query blocks of
-//     one (sequence, head) on one XCD, whose L2 then serves its K and V.
+//     one (sequence, head) on one XCD, whose L2 then serves its K and V;
+//   * the q / k width DQK and the v width DV are separate template parameters: an attention whose
+//     queries and keys are twice as deep as its values (the polar positional scheme of [P2]
+//     "Evaluation record", section "BS PolarFormer...", part "Ported, and what it actually bought",
+//     which asks for a fused attention that accepts v narrower than q) runs in the same loop.
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -56,23 +60,27 @@ constexpr int kKeysPerTile = 64;   // 128 halves the waits per key but leaves 2 
 // LDS rows of 128 bytes (8 chunks of 16): chunk c of row r sits in slot c ^ ((r >> 1) & 7), so any
 // 16 consecutive rows read at one chunk cover all 64 banks.
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// K rows of KCH chunks: 4 or 8 chunks (64- or 128-byte rows) take swz8 modulo KCH; 256-byte rows
+// (16 chunks) start on the same bank, so chunk c of row r sits in slot c ^ (r & 15)
+template <int KCH>
+__device__ __forceinline__ int kswz(int r) { return KCH >= 16 ? (r & 15) : swz8(r) % KCH; }
 // Key order inside a 32-key S^T tile: the A operand row m holds key perm(m) (bits 2 and 3 swapped),
 // which puts the 8 probabilities a lane feeds to one P.V step on 8 consecutive keys.
 __device__ __forceinline__ int perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <typename T, int DH, int KT>
+template <typename T, int DQK, int DV, int KT>
 __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   static_assert(KT % 32 == 0, "keys per tile");
   constexpr int RT = KT / 32;                // 32-key row tiles of S^T per key tile
-  constexpr int KROWB = DH * 2;              // bytes per K row
+  constexpr int KROWB = DQK * 2;             // bytes per K row
   constexpr int KCH = KROWB / 16;            // 16-byte chunks per K row
   constexpr int VROWB = KT * 2;              // bytes per V^T row (KT keys)
   constexpr int VCH = VROWB / 16;            // 16-byte chunks per V^T row
-  constexpr int KBYTES = KT * KROWB, VBYTES = DH * VROWB;
+  constexpr int KBYTES = KT * KROWB, VBYTES = DV * VROWB;
   constexpr int STAGE = KBYTES + VBYTES;
   constexpr int KLD = KBYTES / (256 * 16), VLD = VBYTES / (256 * 16);   // loads per thread per stage
-  constexpr int KSTEPS = DH / 16;            // 32x32x16 steps over dh for S
-  constexpr int DT = DH / 32;                // 32-row d tiles of O^T
+  constexpr int KSTEPS = DQK / 16;           // 32x32x16 steps over the q / k width for S
+  constexpr int DT = DV / 32;                // 32-row d tiles of O^T
   static_assert(KLD >= 1 && VLD >= 1, "tile loader");
   using frag = typename Frag<T>::type;
   typedef typename Frag<T>::half_type h4;
@@ -89,22 +97,22 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   const int seq = sh / L.heads, h = sh - seq * L.heads;
   const int n = L.n, npad = L.npad;
   const int q0 = qb * 128 + w * 32;
-  const size_t base = (size_t)sh * (size_t)npad * DH;
+  const size_t base = (size_t)sh * (size_t)npad * DQK, vbase = (size_t)sh * (size_t)npad * DV;
   const char* Qg = (const char*)((const T*)L.q + base);
   const char* Kg = (const char*)((const T*)L.k + base);
-  const char* Vg = (const char*)((const T*)L.v + base);     // V^T [DH][npad]
+  const char* Vg = (const char*)((const T*)L.v + vbase);    // V^T [DV][npad]
 
   // this thread's DMA chunks: K slot c -> key c / KCH, physical chunk c % KCH holds logical chunk
   // (c % KCH) ^ (key % KCH); V^T slot c -> dim c / 8, 8 keys per chunk, same permutation by dim
   // K [npad][DH] and V^T [DH][npad] of this (sequence, head) as buffers
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kg, (uint32_t)(npad * DH * 2));
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vg, (uint32_t)(npad * DH * 2));
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kg, (uint32_t)(npad * DQK * 2));
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vg, (uint32_t)(npad * DV * 2));
   int ksrc[KLD], kdst[KLD];
 #pragma unroll
   for (int j = 0; j < KLD; ++j) {
     const int c = j * 256 + threadIdx.x;
     const int row = c / KCH, pc = c % KCH;
-    ksrc[j] = row * KROWB + ((pc ^ (swz8(row) % KCH)) << 4);
+    ksrc[j] = row * KROWB + ((pc ^ kswz<KCH>(row)) << 4);
     kdst[j] = (j * 256 + w * 64) * 16;
   }
   int vsrc[VLD], vdst[VLD];
@@ -124,11 +132,17 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   };
 
   // the lane's gate, requested first (read at the end it would wait a memory round trip there)
-  const float gate = q0 + l32 < n ? L.gates[((size_t)seq * L.frames + q0 + l32) * L.heads + h] : 0.f;
+  const float gate = q0 + l32 < n ? (L.gates ? L.gates[((size_t)seq * L.frames + q0 + l32) * L.heads + h] : 1.f) : 0.f;
   // q fragments: B operand of S^T = K Q^T; lane holds query q0 + l32, dims 16*ks + 8*g .. +7
   frag qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *(const frag*)(Qg + ((size_t)(q0 + l32) * DH + 16 * ks + 8 * g) * 2);
+  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *(const frag*)(Qg + ((size_t)(q0 + l32) * DQK + 16 * ks + 8 * g) * 2);
+  if (L.q_mul != 0.0f) {   // q not yet in log2 units: scaled once here, rounded to T
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = cvt<T>(tof<T>(qf[ks][e]) * L.q_mul);
+  }
 
   f32x16 o[DT];
 #pragma unroll
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int lc = 2 * ks + g;
-        const frag a = *(const frag*)(st + row * KROWB + ((lc ^ (swz8(row) % KCH)) << 4));
+        const frag a = *(const frag*)(st + row * KROWB + ((lc ^ kswz<KCH>(row)) << 4));
         if (ks == 0) s[r] = mma32c(a, qf[0], negm);
         else mma32(s[r], a, qf[ks]);
       }
@@ -222,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   if (q >= n) return;
   const size_t row = (size_t)seq * L.frames + q;
   const float scale = gate / lsum;
-  T* dst = (T*)L.o + row * (L.heads * DH) + h * DH;
+  T* dst = (T*)L.o + row * (L.heads * DV) + h * DV;
 #pragma unroll
   for (int d = 0; d < DT; ++d)
 #pragma unroll
@@ -237,17 +251,24 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
 template <typename T>
 hipError_t launch_t(const AttnLaunch& L, hipStream_t stream) {
   dim3 grid((L.npad / 128) * L.heads * L.seqs), block(256);
-  if (L.dh == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 64, kKeysPerTile>), grid, block, 0, stream, L);
-  else if (L.dh == 32) hipLaunchKernelGGL((attn_time2_kernel<T, 32, kKeysPerTile>), grid, block, 0, stream, L);
+  const int dv = L.dv ? L.dv : L.dh;
+  if (L.dh == 64 && dv == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 64, 64, kKeysPerTile>), grid, block, 0, stream, L);
+  else if (L.dh == 32 && dv == 32) hipLaunchKernelGGL((attn_time2_kernel<T, 32, 32, kKeysPerTile>), grid, block, 0, stream, L);
+  else if (L.dh == 128 && dv == 64) hipLaunchKernelGGL((attn_time2_kernel<T, 128, 64, kKeysPerTile>), grid, block, 0, stream, L);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool attention_time2_supported(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 32 && dv == 32) || (dqk == 128 && dv == 64);
+}
+
 hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream) {
-  // q must carry log2(e): scores arrive in log2 units
-  if (L.npad % 128 || L.axis != 0 || L.scale_log2 != 1.0f) return hipErrorInvalidValue;
+  // q must carry log2(e) (and the score scale), or q_mul must bring it
+  if (L.npad % 128 || L.npad < L.n || L.n < 1 || L.axis != 0 || L.scale_log2 != 1.0f) return hipErrorInvalidValue;
+  if (!attention_time2_supported(L.dh, L.dv ? L.dv : L.dh)) return hipErrorInvalidValue;
   switch (L.dtype) {
     case DT_F16: return launch_t<f16>(L, stream);
     case DT_BF16: return launch_t<bf16>(L, stream);

@@ -141,11 +141,17 @@ struct AttnLaunch {
   void* o;                  // [rows][H*dh]
   int32_t n, npad, seqs, heads, dh, frames, batch;
   float scale_log2;         // dh^-1/2 * log2(e) when the scale is not folded; 1*log2(e) otherwise
+  // 16-bit time kernel only: v width when it differs from the q / k width dh (0: dh), and a factor
+  // applied to q as it is loaded (0: none, q arrives in log2 units with its scale, as the
+  // projection writes it); gates may be NULL there (every gate 1)
+  int32_t dv;
+  float q_mul;
 };
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t stream);
 // Time axis, 16-bit operands: v must be V^T [seqs][H][dh][npad] (the 16-bit q/k/v projection writes
 // it that way for the time axis); npad % 128 == 0.
 hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream);
+bool attention_time2_supported(int dqk, int dv);
 
 // y = gelu(x) elementwise with the device GELU of the feed-forward epilogues (test surface).
 hipError_t launch_gelu(const float* x, float* y, int n, hipStream_t stream);

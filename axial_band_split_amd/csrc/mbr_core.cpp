@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -157,7 +158,8 @@ struct mbr_core {
   GemmGroup* groups = nullptr;
   GemmTile* tiles = nullptr;
   int g_embed = 0, t_embed = 0, n_embed = 0;
-  std::vector<std::vector<int>> g_mask, t_mask, n_mask;  // [stem][layer] group start, tile start, tile count
+  // mask head per layer: tile start and count of its one grouped launch over stems x bands
+  std::vector<int> t_mask, n_mask;
   char* tables_dev = nullptr;
 };
 
@@ -230,19 +232,20 @@ int setup_tables_and_groups(mbr_core* c) {
       tiles[c->t_embed + x * per + std::min(x, rem) + slot] = t[i];
     }
   }
+  // mask head: one grouped launch per layer covering every stem and band (a band's stems adjacent,
+  // so at the first layer they share the A panel of that band's rows).  Hidden layers of stem s
+  // live at band block s * NB + i of H1 / H2; the first layer reads x (shared by the stems).
   const int nl = cfg.mask_depth + 1;
-  c->g_mask.assign(cfg.num_stems, std::vector<int>(nl));
-  c->t_mask.assign(cfg.num_stems, std::vector<int>(nl));
-  c->n_mask.assign(cfg.num_stems, std::vector<int>(nl));
-  for (int s = 0; s < cfg.num_stems; ++s) {
-    for (int j = 0; j < nl; ++j) {
-      c->g_mask[s][j] = (int)groups.size();
-      c->t_mask[s][j] = (int)tiles.size();
-      for (int i = 0; i < c->NB; ++i) {
+  c->t_mask.assign(nl, 0);
+  c->n_mask.assign(nl, 0);
+  for (int j = 0; j < nl; ++j) {
+    c->t_mask[j] = (int)tiles.size();
+    for (int i = 0; i < c->NB; ++i) {
+      for (int s = 0; s < cfg.num_stems; ++s) {
         GemmGroup g{};
         const int K = j == 0 ? c->D : c->MH;
         g.a_off0 = 0;
-        g.a_offb = (int64_t)i * K;
+        g.a_offb = (int64_t)(j == 0 ? i : s * c->NB + i) * K;
         g.b_off = (int64_t)c->mw[s].wband[j][i];
         g.bias_off = (int64_t)c->mw[s].bband[j][i];
         g.K = K;
@@ -251,8 +254,8 @@ int setup_tables_and_groups(mbr_core* c) {
         if (j < nl - 1) {
           g.N = c->MH;
           g.c_off0 = 0;
-          g.c_offb = (int64_t)i * c->MH;
-          g.e0 = i;
+          g.c_offb = (int64_t)(s * c->NB + i) * c->MH;
+          g.e0 = i;          // row statistics of x (the first layer's row scale) are per band
         } else {
           g.N = 2 * c->wp[i];
           g.c_off0 = 0;
@@ -263,8 +266,8 @@ int setup_tables_and_groups(mbr_core* c) {
         groups.push_back(g);
         add_tiles((int)groups.size() - 1, g.N, j < nl - 1 ? c->v_mask : c->v_glu);
       }
-      c->n_mask[s][j] = (int)tiles.size() - c->t_mask[s][j];
     }
+    c->n_mask[j] = (int)tiles.size() - c->t_mask[j];
   }
 
   // one device block for all tables
@@ -474,7 +477,8 @@ int alloc_workspace(mbr_core* c) {
   size_t oX = place(NT * c->D * 4), oXH = place(NT * c->D * esz), oG = place(NT * c->H * 4),
          oU = place(BT * c->kpad_total * esz), oqt = place(attn_t), okt = place(attn_t), ovt = place(attn_t),
          oqb = place(attn_b), okb = place(attn_b), ovb = place(attn_b), oO = place(NT * c->I * esz),
-         oH1 = place(NT * std::max(c->FF, c->MH) * esz), oH2 = place(NT * c->MH * esz),
+         oH1 = place(NT * std::max(c->FF, c->cfg.num_stems * c->MH) * esz),
+         oH2 = place(NT * c->cfg.num_stems * c->MH * esz),
          oM = place((size_t)c->cfg.num_stems * BT * c->total * 4);
   size_t oSA = place(NT * kSsStride * 4), oSB = place(NT * kSsStride * 4), oSC = place(NT * kSsStride * 4);
   size_t oP = place(c->use_block ? block_part_bytes(c->D, (int64_t)NT, c->ncu) : 0);
@@ -754,37 +758,35 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   }
 
   const int nlay = cfg.mask_depth + 1;
-  for (int st = 0; st < cfg.num_stems; ++st) {
-    const void* src = c->XH;
-    for (int j = 0; j < nlay; ++j) {
-      GemmLaunch gm{};
-      gm.dtype = dt;
-      gm.A = src;
-      gm.B = W;
-      gm.bias = c->fdev;
-      gm.M = BT;
-      gm.groups = c->groups;
-      gm.tiles = c->tiles + c->t_mask[st][j];
-      gm.n_tiles = c->n_mask[st][j];
-      if (j < nlay - 1) {
-        void* dst = (j % 2 == 0) ? c->H1 : c->H2;
-        gm.epi = EPI_TANH;
-        gm.C = dst;
-        gm.ldc = c->MH;
-        src = dst;
-        if (fused && !c->use_block && j == 0) {   // the last Transformer's output norm, as a row scale
-          gm.rowss = c->ssA;
-          gm.ss_parts = parts;
-          gm.rs_mul = sqrtD;
-        }
-      } else {
-        gm.epi = EPI_GLU;
-        gm.C = c->Mglu;
-        gm.glu_total = c->total;
-        gm.glu_frames = c->T;
+  const void* src = c->XH;
+  for (int j = 0; j < nlay; ++j) {
+    GemmLaunch gm{};
+    gm.dtype = dt;
+    gm.A = src;
+    gm.B = W;
+    gm.bias = c->fdev;
+    gm.M = BT;
+    gm.groups = c->groups;
+    gm.tiles = c->tiles + c->t_mask[j];
+    gm.n_tiles = c->n_mask[j];
+    if (j < nlay - 1) {
+      void* dst = (j % 2 == 0) ? c->H1 : c->H2;
+      gm.epi = EPI_TANH;
+      gm.C = dst;
+      gm.ldc = c->MH;
+      src = dst;
+      if (fused && !c->use_block && j == 0) {   // the last Transformer's output norm, as a row scale
+        gm.rowss = c->ssA;
+        gm.ss_parts = parts;
+        gm.rs_mul = sqrtD;
       }
-      LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, gemm(gm, j < nlay - 1 ? c->v_mask : c->v_glu, s));
+    } else {
+      gm.epi = EPI_GLU;
+      gm.C = c->Mglu;
+      gm.glu_total = c->total;
+      gm.glu_frames = c->T;
     }
+    LAUNCH(j < nlay - 1 ? MBR_K_MASK_HIDDEN : MBR_K_MASK_GLU, gemm(gm, j < nlay - 1 ? c->v_mask : c->v_glu, s));
   }
   if (stop_stage == 1000) return MBR_OK;
 
@@ -1036,6 +1038,39 @@ int mbr_k_gemm(int dtype, const void* a, const void* b, const float* bias, void*
   return MBR_OK;
 }
 
+int mbr_attention(int dtype, const void* q, const void* k, const void* vt, const float* gates, void* o, int seqs,
+                  int heads, int n, int npad, int dqk, int dv, float scale, hipStream_t stream) {
+  if (!q || !k || !vt || !o) return fail(MBR_E_ARG, "NULL argument");
+  if (dtype != MBR_F16 && dtype != MBR_BF16) return fail(MBR_E_ARG, "attention: dtype must be MBR_F16 or MBR_BF16");
+  if (seqs < 1 || heads < 1 || n < 1 || npad < n || npad % 128)
+    return fail(MBR_E_ARG, "attention: seqs, heads >= 1, 1 <= n <= npad, npad a multiple of 128");
+  if (!attention_time2_supported(dqk, dv))
+    return fail(MBR_E_ARG, "attention: (dqk, dv) must be (32, 32), (64, 64) or (128, 64)");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(MBR_E_ARG, "attention: scale must be positive and finite");
+  if ((int64_t)seqs * heads * (npad / 128) > INT32_MAX || (int64_t)npad * dqk * 2 > INT32_MAX)
+    return fail(MBR_E_ARG, "attention: sizes too large");
+  AttnLaunch al{};
+  al.dtype = dtype;
+  al.axis = 0;
+  al.q = q;
+  al.k = k;
+  al.v = vt;
+  al.gates = gates;
+  al.o = o;
+  al.n = n;
+  al.npad = npad;
+  al.seqs = seqs;
+  al.heads = heads;
+  al.dh = dqk;
+  al.dv = dv;
+  al.frames = n;
+  al.batch = 1;
+  al.scale_log2 = 1.0f;
+  al.q_mul = scale * 1.4426950408889634f;   // scores in log2 units for the exponentials
+  HIP_TRY(launch_attention_time2(al, stream));
+  return MBR_OK;
+}
+
 int64_t mbr_core_device_bytes(const mbr_core* c) {
   if (!c) return 0;
   return (int64_t)(c->w_bytes + c->f_bytes + c->ws_bytes);
@@ -1089,7 +1124,7 @@ struct SepPlan {
   size_t o_spec = 0, o_masks = 0, o_frames = 0, o_out = 0, o_cnt = 0, bytes = 0;
 };
 
-int plan_separation(const mbr_core* c, int64_t length, int hop, SepPlan* P) {
+int plan_separation(const mbr_core* c, int64_t length, int hop, int64_t stride, SepPlan* P) {
   const mbr_config& cfg = c->cfg;
   if (cfg.io_layout != MBR_IO_FS_T_C) return fail(MBR_E_ARG, "separate: the core must use MBR_IO_FS_T_C");
   if (!stft_supported(cfg.n_fft) || hop < 1 || hop > cfg.n_fft / 2) return fail(MBR_E_ARG, "separate: bad hop / n_fft");
@@ -1101,7 +1136,10 @@ int plan_separation(const mbr_core* c, int64_t length, int hop, SepPlan* P) {
   G.hop = hop;
   G.T = c->T;
   G.chunk = chunk;
-  G.stride = (int64_t)(chunk * 0.9);
+  if (stride < 0 || stride > chunk - chunk / 10)
+    return fail(MBR_E_ARG, "separate: the stride must be 0 (0.9 chunk) or 1 .. chunk - chunk/10 samples (chunk = " +
+                               std::to_string(chunk) + ")");
+  G.stride = stride > 0 ? stride : (int64_t)(chunk * 0.9);
   const int64_t border = chunk - G.stride;
   G.pad = length > 2 * border ? border : 0;
   G.L = length;
@@ -1126,18 +1164,22 @@ int plan_separation(const mbr_core* c, int64_t length, int hop, SepPlan* P) {
 }
 }  // namespace
 
-int64_t mbr_separate_workspace_size(const mbr_core* c, int64_t length, int hop) {
+int64_t mbr_separate_workspace_size_strided(const mbr_core* c, int64_t length, int hop, int64_t stride) {
   if (!c) return fail(MBR_E_ARG, "NULL core");
   SepPlan P;
-  int rc = plan_separation(c, length, hop, &P);
+  int rc = plan_separation(c, length, hop, stride, &P);
   return rc ? rc : (int64_t)P.bytes;
 }
 
-int mbr_separate(mbr_core* c, const float* wave, int64_t length, int hop, void* workspace, float* out,
-                 hipStream_t stream) {
+int64_t mbr_separate_workspace_size(const mbr_core* c, int64_t length, int hop) {
+  return mbr_separate_workspace_size_strided(c, length, hop, 0);
+}
+
+int mbr_separate_strided(mbr_core* c, const float* wave, int64_t length, int hop, int64_t stride, void* workspace,
+                         float* out, hipStream_t stream) {
   if (!c || !wave || !workspace || !out) return fail(MBR_E_ARG, "NULL argument");
   SepPlan P;
-  int rc = plan_separation(c, length, hop, &P);
+  int rc = plan_separation(c, length, hop, stride, &P);
   if (rc) return rc;
   StftGeom& G = P.G;
   G.wave = wave;
@@ -1158,6 +1200,11 @@ int mbr_separate(mbr_core* c, const float* wave, int64_t length, int hop, void* 
   }
   HIP_TRY(launch_finish(G, P.stems, acc, cnt, out, stream));
   return MBR_OK;
+}
+
+int mbr_separate(mbr_core* c, const float* wave, int64_t length, int hop, void* workspace, float* out,
+                 hipStream_t stream) {
+  return mbr_separate_strided(c, wave, length, hop, 0, workspace, out, stream);
 }
 
 void mbr_core_destroy(mbr_core* c) {

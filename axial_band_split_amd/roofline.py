@@ -60,7 +60,7 @@ KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E", "qkv": r"gemm2_kernelIDF16b
               "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
               "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
               "norm": r"norm", "gather": r"gather", "average": r"average",
-              "block": r"block_kernel|block_reduce_kernel"}
+              "block": r"block2?_kernel|block_reduce_kernel"}
 MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block")
 HBM_KINDS = ("gather", "average", "attn_band", "norm")
 
@@ -78,9 +78,10 @@ def flops_per_launch(s: Shape) -> Dict[str, float]:
         "out_proj": 2.0 * N * I * D,
         "ffn1": 2.0 * N * D * s.FF,
         "ffn2": 2.0 * N * s.FF * D,
-        "mask_hidden_first": 2.0 * BT * s.NB * D * s.MH,
-        "mask_hidden_next": 2.0 * BT * s.NB * s.MH * s.MH,
-        "mask_glu": 2.0 * BT * s.MH * 2 * s.total_width,
+        # the mask head: one launch per layer covers every stem
+        "mask_hidden_first": 2.0 * s.stems * BT * s.NB * D * s.MH,
+        "mask_hidden_next": 2.0 * s.stems * BT * s.NB * s.MH * s.MH,
+        "mask_glu": 2.0 * s.stems * BT * s.MH * 2 * s.total_width,
         # out-projection + feed-forward of one Transformer in one kernel (16-bit path)
         "block": 2.0 * N * I * D + 4.0 * N * D * s.FF,
     }
@@ -92,7 +93,7 @@ def flops_forward(s: Shape) -> Dict[str, float]:
     L = s.depth
     per_axis = f["qkv"] + f["norm_gates"] + f["out_proj"] + f["ffn1"] + f["ffn2"]
     trunk = 2 * L * per_axis + L * (f["attn_time"] + f["attn_band"])
-    mask = s.stems * (f["mask_hidden_first"] + (s.mask_depth - 1) * f["mask_hidden_next"] + f["mask_glu"])
+    mask = f["mask_hidden_first"] + (s.mask_depth - 1) * f["mask_hidden_next"] + f["mask_glu"]
     return {"embed": f["embed"], "trunk": trunk, "mask": mask, "total": f["embed"] + trunk + mask,
             "attn": L * (f["attn_time"] + f["attn_band"])}
 

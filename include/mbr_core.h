@@ -233,6 +233,27 @@ int mbr_k_gemm_variants(void);
  */
 int mbr_k_gelu(const float* x_dev, float* y_dev, int n, hipStream_t stream);
 
+/*
+ * Gated scaled dot-product attention on 16-bit operands with the flash kernel of the core's time
+ * axis (online softmax in fp32, the scores never stored), for q / k of width dqk and v of width dv:
+ *   o[s][t][h*dv + d] = gate[s*n + t][h] * sum_j softmax_j(scale * q[s][h][t] . k[s][h][j]) v[s][h][j][d]
+ * dv may be half of dqk: the attention of [P2] "Evaluation record", section "BS PolarFormer: the same
+ * quality for a quarter of the arithmetic", part "Ported, and what it actually bought", whose polar
+ * positional scheme doubles the depth of q and k and leaves v alone, and which asks for a fused
+ * attention that accepts v narrower than q (the positional transform itself is the caller's: q and
+ * k arrive transformed).
+ *   q_dev, k_dev   [seqs][heads][npad][dqk] in dtype (MBR_F16 or MBR_BF16).
+ *   vt_dev         [seqs][heads][dv][npad] in dtype: v transposed, positions contiguous.
+ *   gates_dev      [seqs * n][heads] float32, or NULL for gates of 1.
+ *   o_dev          [seqs][n][heads * dv] in dtype (written).
+ * 1 <= n <= npad, npad a multiple of 128; (dqk, dv) = (32, 32), (64, 64) or (128, 64); scale > 0
+ * (dqk^-1/2 for the usual scaling).  Rows n .. npad-1 of q and k and columns n .. npad-1 of vt are
+ * read and must hold finite values (those keys get probability 0, but 0 x inf is not 0).  Returns
+ * MBR_E_ARG on bad sizes, MBR_E_HIP if the launch fails.  Asynchronous on `stream`.
+ */
+int mbr_attention(int dtype, const void* q_dev, const void* k_dev, const void* vt_dev, const float* gates_dev,
+                  void* o_dev, int seqs, int heads, int n, int npad, int dqk, int dv, float scale, hipStream_t stream);
+
 /* Device bytes held by the core (weights + workspace). */
 int64_t mbr_core_device_bytes(const mbr_core* core);
 
@@ -282,6 +303,18 @@ int mbr_istft_masked(const float* stft_repr_dev, const float* masks_dev, int ste
 int64_t mbr_separate_workspace_size(const mbr_core* core, int64_t length, int hop);
 int mbr_separate(mbr_core* core, const float* wave_dev, int64_t length, int hop, void* workspace_dev,
                  float* out_dev, hipStream_t stream);
+/*
+ * mbr_separate with the chunk stride chosen by the caller, in samples: 0 gives int(0.9 * chunk)
+ * (mbr_separate itself); chunk / 2 gives the segmenting of [P4] "Graph" (8 s segments every 4 s,
+ * faded over 0.8 s, the input reflected out at the ends, as the training repository's demix runs
+ * with two overlaps).  Everything else as mbr_separate: the border (reflect pad) is chunk - stride,
+ * the fades chunk / 10, the summed fades divide the sum.  1 <= stride <= chunk - chunk / 10 (so every
+ * sample of the padded track has a chunk of weight 1 over it), else MBR_E_ARG.  The workspace size
+ * depends on the stride.
+ */
+int64_t mbr_separate_workspace_size_strided(const mbr_core* core, int64_t length, int hop, int64_t stride);
+int mbr_separate_strided(mbr_core* core, const float* wave_dev, int64_t length, int hop, int64_t stride,
+                         void* workspace_dev, float* out_dev, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,8 @@ Modules
   mel     Slaney mel bands, binarised incidence, gather and inverse index tables
   model   weight inventory and the vectorised numpy forward (every step in fp64)
   brute   an independent scalar-loop forward for tiny shapes, used to pin ``model``
+  attention  gated attention with q, k wider than v (the polar scheme's shape)
+  pipeline   STFT, mask product, inverse STFT and the chunked overlap-add around the core
 
 Every function cites the page passage it follows.  Pages:
   [P1] "Mel-Band RoFormer — architecture, inference hot path & RTX 3050 feasibility"

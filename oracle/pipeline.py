@@ -5,10 +5,11 @@
 into the frequency axis are the core's input [B, F*S, T, 2]; the core's complex masks multiply
 the original STFT and an inverse STFT returns one waveform per stem.
 [P1] "Verified inference hot path" (chunk arithmetic, steps 3-9): a track is cut into chunks of
-8 s with a stride of 0.9 chunk, reflect-padded by the border (chunk - stride) on both sides when
-it is longer than two borders; each chunk's estimate is weighted by a linear fade window (fade =
-chunk / 10, no fade-in on the first chunk, no fade-out on the last), summed, divided by the summed
-window (clamped at 1e-8), and the padding is cropped.  A tail shorter than a chunk is reflect-
+8 s with a stride of 0.9 chunk (or of half a chunk, the segmenting of [P4] "Graph"), reflect-
+padded by the border (chunk - stride) on both sides when it is longer than two borders; each
+chunk's estimate is weighted by a linear fade window (fade = chunk / 10, no fade-in on the first
+chunk, no fade-out on the last), summed, divided by the summed window (clamped at 1e-8), and the
+padding is cropped.  A tail shorter than a chunk is reflect-
 padded when it holds more than half a chunk of audio, else zero-padded.
 
 Readings where the text leaves a detail open (each also stated in the design notes):
@@ -82,10 +83,16 @@ def apply_masks(z: np.ndarray, masks: np.ndarray) -> np.ndarray:
     return z[None] * m
 
 
-def chunk_plan(length: int, chunk: int):
+def default_stride(chunk: int) -> int:
+    """[P1] "Verified inference hot path" step 3: stride = int(0.9 chunk)."""
+    return int(chunk * 0.9)
+
+
+def chunk_plan(length: int, chunk: int, stride: int | None = None):
     """Chunk arithmetic: (padded length, border applied, [(offset, n_valid, tail_mode)]) where
-    tail_mode is 'full', 'reflect' or 'zero'."""
-    stride = int(chunk * 0.9)
+    tail_mode is 'full', 'reflect' or 'zero'.  stride None: [P1]'s 0.9 chunk; [P4] "Graph" segments
+    every half chunk (8 s every 4 s), with the same border = chunk - stride and fades."""
+    stride = default_stride(chunk) if stride is None else stride
     border = chunk - stride
     pad = border if length > 2 * border else 0
     Lp = length + 2 * pad
@@ -108,12 +115,12 @@ def fade_window(chunk: int, first: bool, last: bool) -> np.ndarray:
 
 
 def separate(wave: np.ndarray, core: Callable[[np.ndarray], np.ndarray], n_fft: int, hop: int, chunk: int,
-             stems: int) -> np.ndarray:
+             stems: int, stride: int | None = None) -> np.ndarray:
     """wave [S, L] -> [stems, S, L]: chunked STFT -> core -> masks x STFT -> iSTFT -> faded overlap-add.
     `core` maps stft_repr [1, F*S, T, 2] to masks [stems, F*S, T, 2]."""
     S, L = wave.shape
-    stride = int(chunk * 0.9)
-    Lp, pad, plan = chunk_plan(L, chunk)
+    stride = default_stride(chunk) if stride is None else stride
+    Lp, pad, plan = chunk_plan(L, chunk, stride)
     x = wave[:, reflect_index(np.arange(Lp) - pad, L)] if pad else wave
     out = np.zeros((stems, S, Lp))
     counter = np.zeros(Lp)

@@ -158,3 +158,36 @@ def test_separation_refuses_a_one_sample_track():
     with pytest.raises(binding.MbrError):
         core.separate(x, 64)
     core.close()
+
+
+@pytest.mark.parametrize("L,stride", [(7000, 1024), (9333, 1024), (2500, 700)])
+def test_strided_separation_matches_oracle_tiny_core(L, stride):
+    """The separation with a chosen stride: half a chunk ([P4] "Graph": segments every half chunk,
+    the border as large), and an odd stride; tiny fp32 core, 2048-sample chunks, two per core call."""
+    w = synth.WORKLOADS["tiny_fp32"].replace(frames=33, batch=2)
+    cfg = binding.config(w)
+    ws = synth.draw_weights(binding.inventory(cfg), w.dtype, seed=0, std=0.1)
+    oc = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads, w.dim_head,
+                      w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
+    x = np.random.default_rng(8).standard_normal((2, L)).astype(np.float32)
+    say(f"[separate] tiny core, L={L}, stride {stride}")
+    core = binding.Core(cfg, ws)
+    got = core.separate(torch.from_numpy(x).cuda(), 64, stride=stride).cpu().numpy()
+    core.close()
+    want = P.separate(x.astype(np.float64), lambda spec: M.forward(spec, oc, ws), 256, 64, 2048, 1, stride=stride)
+    err = rel_l2(got, want)
+    say(f"[separate] rel L2 = {err:.2e}")
+    assert got.shape == want.shape and err < 1e-4
+
+
+def test_separation_refuses_a_stride_past_the_fades():
+    """A stride over chunk - chunk/10 (2048-sample chunks: 1844) would leave samples without a chunk
+    of full weight: 1845 is MBR_E_ARG before anything is launched; 1844 is accepted."""
+    w = synth.WORKLOADS["tiny_fp32"].replace(frames=33, batch=1)
+    cfg = binding.config(w)
+    core = binding.Core(cfg, synth.draw_weights(binding.inventory(cfg), w.dtype, seed=0))
+    assert binding.mbr_separate_workspace_size_strided(core.handle, 5000, 64, 1844) > 0
+    with pytest.raises(binding.MbrError) as e:
+        binding.mbr_separate_workspace_size_strided(core.handle, 5000, 64, 1845)
+    assert e.value.code == binding.MBR_E_ARG
+    core.close()

@@ -123,3 +123,28 @@ def test_mask_product_with_non_unit_masks():
     mr, mi = g[0, f * S + s, t]
     zr, zi = z[s, f, t].real, z[s, f, t].imag
     assert y[0, s, f, t] == complex(zr * mr - zi * mi, zr * mi + zi * mr)
+
+
+def test_segments_every_half_chunk():
+    """[P4] "Graph": 8 s segments every 4 s faded over 0.8 s, the input reflected out at the ends:
+    stride 176400, border (reflect pad) 176400, fades of 35280 samples."""
+    chunk = 44100 * 8
+    Lp, pad, plan = P.chunk_plan(60 * 44100, chunk, chunk // 2)
+    assert pad == 176400 and Lp == 60 * 44100 + 2 * 176400
+    assert [o for o, _, _ in plan][:4] == [0, 176400, 352800, 529200]
+    assert len(plan) == -(-Lp // 176400)
+
+
+@pytest.mark.parametrize("L", [2500, 7000, 9333])
+def test_half_chunk_separation_with_unit_masks_returns_the_track(L):
+    n_fft, hop, chunk = 256, 64, 2048
+    wave = np.random.default_rng(6).standard_normal((2, L))
+
+    def unit_core(spec):
+        m = np.zeros((1,) + spec.shape[1:])
+        m[..., 0] = 1.0
+        return m
+
+    out = P.separate(wave, unit_core, n_fft, hop, chunk, stems=1, stride=chunk // 2)
+    assert out.shape == (1, 2, L)
+    assert np.allclose(out[0], wave, rtol=0, atol=1e-10)
