@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmbr_core.so")
 
 MBR_OK, MBR_E_ARG, MBR_E_CONFIG, MBR_E_DEVICE, MBR_E_HIP, MBR_E_NOMEM = 0, -1, -2, -3, -4, -5
+MBR_ISTFT_NOALLOC_MAX_BYTES = 64 << 20       # the static frame buffer of mbr_istft_masked_noalloc
 
 # Every symbol include/mbr_core.h declares, with (restype, argtypes).
 _SIGS = {
@@ -43,6 +44,8 @@ _SIGS = {
     "mbr_istft_workspace_size": (C.c_int64, [C.c_int, C.c_int, C.c_int, C.c_int]),
     "mbr_istft_masked": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_void_p,
                                    C.c_void_p, C.c_void_p]),
+    "mbr_istft_masked_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int,
+                                           C.c_void_p, C.c_void_p]),
     "mbr_separate_workspace_size": (C.c_int64, [C.c_void_p, C.c_int64, C.c_int]),
     "mbr_separate": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
     "mbr_separate_workspace_size_strided": (C.c_int64, [C.c_void_p, C.c_int64, C.c_int, C.c_int64]),
@@ -208,6 +211,12 @@ def mbr_istft_masked(spec_ptr: int, masks_ptr: int, stems: int, channels: int, l
                      ws_ptr: int, out_ptr: int, stream_ptr: int = 0) -> None:
     _check(lib().mbr_istft_masked(C.c_void_p(spec_ptr), C.c_void_p(masks_ptr), stems, channels, length, n_fft, hop,
                                   C.c_void_p(ws_ptr), C.c_void_p(out_ptr), C.c_void_p(stream_ptr)))
+
+
+def mbr_istft_masked_noalloc(spec_ptr: int, masks_ptr: int, stems: int, channels: int, length: int, n_fft: int,
+                             hop: int, out_ptr: int, stream_ptr: int = 0) -> None:
+    _check(lib().mbr_istft_masked_noalloc(C.c_void_p(spec_ptr), C.c_void_p(masks_ptr), stems, channels, length, n_fft,
+                                          hop, C.c_void_p(out_ptr), C.c_void_p(stream_ptr)))
 
 
 def mbr_separate_workspace_size(h, length: int, hop: int) -> int:

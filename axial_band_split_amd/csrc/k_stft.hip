@@ -13,10 +13,17 @@
 //   * the chunks' estimates are combined by a gather over output samples (at most two chunks and
 //     ceil(n_fft / hop) frames meet at a sample), in stream order between groups of chunks: no
 //     atomics, deterministic.
+#include <mutex>
+
 #include "kcommon.h"
 #include "kernels.h"
 
 namespace mbr {
+
+// Frame buffer of the allocation-free inverse STFT (mbr_istft_masked_noalloc): one copy per GPU,
+// at its own address on each, held until the process ends.  Host code never uses this name as an
+// address: it asks the runtime for the current device's copy (istft_noalloc_scratch).
+static __device__ __align__(256) char scratch[kIstftNoallocBytes];
 
 namespace {
 
@@ -229,6 +236,25 @@ hipError_t launch_finish(const StftGeom& G, int stems, const float* out, const f
   hipLaunchKernelGGL(finish_kernel, dim3((unsigned)((G.L + 255) / 256), stems * G.S), dim3(256), 0, stream, G,
                      stems, out, counter, dst);
   return hipGetLastError();
+}
+
+hipError_t istft_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {   // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_fill0(float* p, int64_t n, hipStream_t stream) {

@@ -208,6 +208,10 @@ hipError_t launch_ola(const StftGeom& G, const float* frames, int stems, int ngr
 hipError_t launch_finish(const StftGeom& G, int stems, const float* out, const float* counter, float* dst,
                          hipStream_t stream);
 hipError_t launch_fill0(float* p, int64_t n, hipStream_t stream);
+// Bytes of the static frame buffer of the allocation-free inverse STFT, and the current device's
+// address of it (looked up once per device).
+constexpr int64_t kIstftNoallocBytes = (int64_t)64 << 20;
+hipError_t istft_noalloc_scratch(void** ptr);
 int64_t block_stream_elems(int D, int I, int FF);
 hipError_t launch_block(const BlockLaunch& L, hipStream_t stream);
 

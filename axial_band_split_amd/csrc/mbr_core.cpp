@@ -1117,6 +1117,33 @@ int mbr_istft_masked(const float* spec, const float* masks, int stems, int chann
   return MBR_OK;
 }
 
+int mbr_istft_masked_noalloc(const float* spec, const float* masks, int stems, int channels, int64_t length,
+                             int n_fft, int hop, float* out, hipStream_t stream) {
+  if (!spec || !masks || !out) return fail(MBR_E_ARG, "NULL argument");
+  if (channels < 1 || stems < 1 || length < 2 || !stft_supported(n_fft) || hop < 1 || hop > n_fft / 2)
+    return fail(MBR_E_ARG, "istft: bad sizes");
+  const int64_t T = 1 + length / hop;
+  const int64_t need = (int64_t)stems * channels * T * n_fft * 4;
+  if (need > MBR_ISTFT_NOALLOC_MAX_BYTES)
+    return fail(MBR_E_ARG, "istft (no allocation): stems * channels * frames * n_fft * 4 = " + std::to_string(need) +
+                               " bytes exceeds the static buffer of " + std::to_string((int64_t)MBR_ISTFT_NOALLOC_MAX_BYTES));
+  static_assert(MBR_ISTFT_NOALLOC_MAX_BYTES == kIstftNoallocBytes, "header and library agree on the buffer size");
+  void* frames = nullptr;
+  HIP_TRY(istft_noalloc_scratch(&frames));
+  StftGeom G{};
+  G.S = channels;
+  G.n_fft = n_fft;
+  G.hop = hop;
+  G.T = (int32_t)T;
+  G.no_fade = 1;
+  G.L = G.Lp = G.chunk = G.stride = length;
+  // every element of the frames this call reads is written by its own istft_frames launch first
+  HIP_TRY(launch_istft_frames(G, 1, spec, masks, stems, (float*)frames, stream));
+  HIP_TRY(launch_fill0(out, (int64_t)stems * channels * length, stream));
+  HIP_TRY(launch_ola(G, (const float*)frames, stems, 1, 0, length, out, nullptr, stream));
+  return MBR_OK;
+}
+
 namespace {
 struct SepPlan {
   StftGeom G{};

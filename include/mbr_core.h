@@ -284,6 +284,22 @@ int64_t mbr_istft_workspace_size(int channels, int n_fft, int frames, int stems)
 int mbr_istft_masked(const float* stft_repr_dev, const float* masks_dev, int stems, int channels, int64_t length,
                      int n_fft, int hop, void* workspace_dev, float* out_dev, hipStream_t stream);
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): mbr_istft_masked with no workspace argument.  The
+ * frame buffer is a static device array of MBR_ISTFT_NOALLOC_MAX_BYTES bytes in the library, one
+ * copy per GPU, held until the process ends; its address is looked up on the first call on each
+ * device.  Arguments, layouts and results as mbr_istft_masked (the same kernels; the outputs are
+ * bitwise equal).  Calls allocate nothing and clear nothing they do not write first.  Every call
+ * on one GPU shares that GPU's buffer, so calls that overlap on one GPU (different streams or
+ * threads without ordering between them) race and give wrong results: order them.
+ * Returns MBR_E_ARG when stems * channels * (1 + length / hop) * n_fft * 4 exceeds
+ * MBR_ISTFT_NOALLOC_MAX_BYTES (64 MiB: about 41 s of stereo audio at n_fft 2048, hop 441, one
+ * stem) or on bad sizes, MBR_E_HIP if the buffer lookup or a launch fails.
+ */
+#define MBR_ISTFT_NOALLOC_MAX_BYTES ((int64_t)64 << 20)
+int mbr_istft_masked_noalloc(const float* stft_repr_dev, const float* masks_dev, int stems, int channels,
+                             int64_t length, int n_fft, int hop, float* out_dev, hipStream_t stream);
+/*
  * Separation of one track by chunks ([P1] "Verified inference hot path", steps 3-9): chunk =
  * (core frames - 1) * hop samples, stride int(0.9 * chunk), border = chunk - stride; a track
  * longer than two borders is reflect-padded by one border on each side; each chunk (its tail
