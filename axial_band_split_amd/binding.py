@@ -53,7 +53,7 @@ _SIGS = {
                                        C.c_void_p]),
 }
 KERNEL_KINDS = ("gather", "embed", "norm", "qkv", "attn_time", "attn_band", "out_proj", "ffn1", "ffn2",
-                "mask_hidden", "mask_glu", "average", "block")
+                "mask_hidden", "mask_glu", "average", "block", "band_attn")
 SYMBOLS = tuple(_SIGS)
 
 

@@ -1,0 +1,324 @@
+// The band-axis attention of a Transformer in one kernel (fp16 / bf16): the q, k, v projection of
+// one head for the bands of four frames, the attention over the bands of each frame, and the gated
+// output, with q, k and v never leaving the compute unit.
+//
+// ([P1] "The two transformers are not the same shape": the band Transformer runs one sequence per
+// frame over the bands, positions = band index; "Per Attention layer": x^ W_qkv^T split head-major,
+// rotary on q and k, softmax(q k^T / sqrt(dh)) v per head, times sigmoid(x^ W_g^T + b_g) per head.
+// The scale 1/sqrt(dh) is folded into W_q at create; q is multiplied by log2 e here so the
+// exponentials are base 2.)
+//
+// Workgroup = (4 frames, head h), 8 waves.  The 4 x 64 band slots of the frames (bands >= NB are
+// padding rows, read as a valid row and masked as keys) are the rows of a 256 x 192 x D product
+// against the head's rows of W_qkv ([q_h | k_h | v_h]); K goes through a 3-stage LDS ring by 16-byte
+// direct loads, as in the GEMM.  Wave (f, r) owns the 32 band slots 32r .. 32r+31 of frame f and all
+// 192 columns (six 32 x 32 tiles on v_mfma_f32_32x32x16):
+//   * the q and k tiles are taken transposed (features x tokens), so a lane holds one token and four
+//     consecutive features per group: the rotary pairs are in the lane, and the accumulator read in
+//     8-element halves is directly an operand of the score product S^T = K Q^T (the feature order
+//     inside each 16-feature step is permuted the same way for q and k, which a dot product allows);
+//   * the v tiles are taken as tokens x features, which read the same way are the V^T operand of
+//     O^T = V^T P^T whose key order matches the probabilities straight from the S^T accumulators;
+//   * the two waves of a frame swap their keys' k and v fragments through LDS (8 KB each);
+//   * the gate of each token is a dot product on the vector units, read from the same LDS tiles of
+//     x^ during the K loop (two lanes per token, half the K step each).
+// The softmax runs over one tile of 64 keys (the 60 bands of a frame) in registers; the output goes
+// out through a per-wave LDS staging as 16-byte rows.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mbr {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mma32(f32x16& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16-byte chunks of a 64-byte LDS row, XOR-permuted so the 32 rows of a fragment read spread over
+// the banks (the GEMM's layout)
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+constexpr float kNegBig = -1e30f;
+
+constexpr int kRows = 256;               // 4 frames x 64 band slots
+constexpr int kCols = 192;               // [q_h | k_h | v_h], dh = 64
+constexpr int kStage = (kRows + kCols) * 64;   // one K step of 32: 28 KB
+constexpr int kNS = 3;
+constexpr int kExch = 8 * 8192;          // per wave: its keys' 4 k and 4 v fragments
+constexpr int kOut = 8 * 4096;           // per wave: 32 tokens x 64 outputs, 16-bit
+constexpr int kLds = (kNS * kStage > kExch + kOut ? kNS * kStage : kExch + kOut);
+
+template <typename T>
+__global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
+  using frag = typename Frag<T>::type;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) float wg[1024];   // the head's gate weights (D <= 1024)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int r32 = lane & 31, hl = lane >> 5;
+  const int fl = wu >> 1, half = wu & 1;                    // frame of the group, band half
+  const int D = L.D, I = L.heads * 64, BT = L.BT, NB = L.NB;
+  // workgroups are dealt round-robin to the 8 XCDs: one contiguous run each, so the 8 heads of a
+  // frame group (the same rows of x^) share an L2
+  const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int logical = xcd * per + min(xcd, rem) + slot;
+  const int h = logical % L.heads, f0 = (logical / L.heads) * 4;
+
+  for (int i = tid; i < D; i += 512) wg[i] = tof<T>(((const T*)L.W)[(size_t)(3 * I + h) * D + i]);
+  __syncthreads();
+
+  // ---- loader.  A row rho: frame f0 + rho/64, band slot rho%64 -> token slot*BT + frame (padding
+  // rows read the nearest valid token); B row c: W_qkv row h*64 + c of q, k or v.
+  const int64_t rowb = (int64_t)D * 2;
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc_uniform(L.XH, (uint32_t)((int64_t)NB * BT * rowb));
+  const __amdgpu_buffer_rsrc_t brs = buffer_rsrc_uniform(L.W, (uint32_t)((int64_t)(3 * I + 64) * rowb));
+  int voff[4];
+  bool bload2 = false;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {            // A: 1024 chunks
+    const int c = j * 512 + tid, row = c >> 2, pc = c & 3;
+    const int f = min(f0 + (row >> 6), BT - 1), s = min(row & 63, NB - 1);
+    voff[j] = (int)(((int64_t)s * BT + f) * rowb) + ((pc ^ swz(row)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {            // B: 768 chunks (the second round: waves 0..3)
+    const int c = j * 512 + tid, row = min(c >> 2, kCols - 1), pc = c & 3;
+    const int wrow = (row >> 6) * I + h * 64 + (row & 63);
+    voff[2 + j] = (int)(wrow * rowb) + ((pc ^ swz(row)) << 4);
+  }
+  bload2 = wu < 4;
+  auto issue = [&](int ks) {
+    char* base = smem + (ks % kNS) * kStage;
+    const int ko = ks * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) buffer_dma16(ars, voff[j], ko, base + (j * 8 + wu) * 1024);
+    buffer_dma16(brs, voff[2], ko, base + kRows * 64 + wu * 1024);
+    if (bload2) buffer_dma16(brs, voff[3], ko, base + kRows * 64 + (8 + wu) * 1024);
+  };
+
+  // ---- the 256 x 192 product; this wave: rows 64 fl + 32 half + (0..31), all six column tiles.
+  // Tiles 0..3 (q, k) as C^T = W X^T, tiles 4, 5 (v) as C = X W^T.
+  f32x16 acc[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  float gdot = 0.f;                         // gate: this lane's token, K half hl of every step
+  const int arow = 64 * fl + 32 * half + r32;
+  const int nk = D >> 5;
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) {                      // at most the next stage's loads outstanding (3 or 4)
+      if (bload2) wait_vm<4>();
+      else wait_vm<3>();
+    } else {
+      wait_vm<0>();
+    }
+    block_barrier();
+    if (ks + 2 < nk) issue(ks + 2);         // the slot of step ks-1, read by every wave before the barrier
+    const char* st = smem + (ks % kNS) * kStage;
+    frag a[2], b[2][6];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int lc = 2 * kh + hl;
+      a[kh] = *(const frag*)(st + arow * 64 + ((lc ^ swz(arow)) << 4));
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const int brow = 32 * j + r32;
+        b[kh][j] = *(const frag*)(st + kRows * 64 + brow * 64 + ((lc ^ swz(brow)) << 4));
+      }
+    }
+    // gate: elements 16 hl .. 16 hl + 15 of this step for the lane's token (chunks 2 hl, 2 hl + 1)
+    {
+      const frag g0 = *(const frag*)(st + arow * 64 + (((2 * hl) ^ swz(arow)) << 4));
+      const frag g1 = *(const frag*)(st + arow * 64 + (((2 * hl + 1) ^ swz(arow)) << 4));
+      const float* wk = wg + ks * 32 + 16 * hl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gdot = fmaf(tof<T>(g0[e]), wk[e], gdot);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gdot = fmaf(tof<T>(g1[e]), wk[8 + e], gdot);
+    }
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma32(acc[j], b[kh][j], a[kh]);
+#pragma unroll
+      for (int j = 4; j < 6; ++j) mma32(acc[j], a[kh], b[kh][j]);
+    }
+  }
+
+  // ---- row scale (x^ not yet normalised: sqrt(D) / |x|), rotary on q and k, q in log2 units
+  const int slot_me = 32 * half + r32;                  // this lane's band slot (token of tiles 0..3)
+  const int fr = f0 + fl;
+  const int64_t token = (int64_t)min(slot_me, NB - 1) * BT + min(fr, BT - 1);
+  float sc = 1.0f;
+  if (L.rowss) {
+    const float4* p = (const float4*)(L.rowss + token * kSsStride);
+    const float4 x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
+    const float ss = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w)) + ((x2.x + x2.y) + (x2.z + x2.w)) +
+                     ((x3.x + x3.y) + (x3.z + x3.w));
+    sc = L.rs_mul / fmaxf(sqrtf(ss), kNormEps);
+  }
+  gdot += __shfl_xor(gdot, 32, 64);
+  const float gate = sigmoidf_(gdot * sc + L.gate_bias[h]);
+  // q (tiles 0, 1) and k (tiles 2, 3): element v is feature 32 (j%2) + 8 (v/4) + 4 hl + v%4 of the token
+  // slot_me; pairs (2p, 2p+1) are elements (4g, 4g+1), (4g+2, 4g+3)
+  frag qf[4], kf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * (j & 1) + 8 * g4 + 4 * hl;
+      const float2 cs = *(const float2*)(L.cos + slot_me * 32 + (d >> 1));
+      const float2 sn = *(const float2*)(L.sin + slot_me * 32 + (d >> 1));
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[j][4 * g4 + e] * sc;
+      float y[4];
+      y[0] = x[0] * cs.x - x[1] * sn.x;
+      y[1] = x[0] * sn.x + x[1] * cs.x;
+      y[2] = x[2] * cs.y - x[3] * sn.y;
+      y[3] = x[2] * sn.y + x[3] * cs.y;
+      const float m = j < 2 ? L.q_mul : 1.0f;
+      frag& dst = j < 2 ? qf[2 * (j & 1) + (g4 >> 1)] : kf[2 * (j & 1) + (g4 >> 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[4 * (g4 & 1) + e] = cvt<T>(y[e] * m);
+    }
+  }
+  // v (tiles 4, 5): lane = feature 32 (j-4) + r32, element v = token slot 32 half + 8 (v/4) + 4 hl + v%4:
+  // the row scale of each element's token, from the lane holding that token
+  frag vf[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float s = L.rowss ? __shfl(sc, 8 * (v >> 2) + 4 * hl + (v & 3), 64) : 1.0f;
+      vf[j][v >> 3][v & 7] = cvt<T>(acc[4 + j][v] * s);
+    }
+
+  // ---- swap keys with the other half of the frame: this wave's k (as S^T A operand) and v (as V^T
+  // A operand) fragments, 8 x 1 KB, lanes contiguous
+  block_barrier();                          // every wave is done with the ring
+  char* mine = smem + wu * 8192 + lane * 16;
+  const char* theirs = smem + (wu ^ 1) * 8192 + lane * 16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) *(frag*)(mine + s * 1024) = kf[s];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) *(frag*)(mine + (4 + 2 * j + s) * 1024) = vf[j][s];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();
+  frag kp[4], vp[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kp[s] = *(const frag*)(theirs + s * 1024);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) vp[j][s] = *(const frag*)(theirs + (4 + 2 * j + s) * 1024);
+
+  // ---- S^T (64 keys x this wave's 32 queries): key tile t holds the slots of half t
+  f32x16 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[t][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) mma32(st[t], (t == half) ? kf[s] : kp[s], qf[s]);
+  }
+  // keys past the last band get probability 0; scores are in log2 units
+  float mx = kNegBig;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
+      if (key >= NB) st[t][v] = kNegBig;
+      mx = fmaxf(mx, st[t][v]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float lsum = 0.f;
+  frag pf[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(st[t][v] - mx);
+      lsum += p;
+      pf[2 * t + (v >> 3)][v & 7] = cvt<T>(p);
+    }
+  lsum += __shfl_xor(lsum, 32, 64);
+  // ---- O^T = V^T P^T: key step ks (16 keys) is half ks/2's v fragment ks%2
+  f32x16 o[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[j][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) mma32(o[j], ((ks >> 1) == half) ? vf[j][ks & 1] : vp[j][ks & 1], pf[ks]);
+  }
+
+  // ---- gated output: stage [token][64] 16-bit rows per wave, then 16-byte stores of whole rows
+  const float scale = gate / lsum;
+  char* ob = smem + kExch + wu * 4096;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      typename Vec4<T>::type q4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q4[e] = cvt<T>(o[j][4 * g4 + e] * scale);
+      const int d = 32 * j + 8 * g4 + 4 * hl;
+      *(typename Vec4<T>::type*)(ob + r32 * 128 + ((((d >> 3) ^ (r32 & 7)) << 4) | ((d & 4) << 1))) = q4;
+    }
+  // each lane's own staging rows only: the wave reads back what it wrote (in order, lgkmcnt)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int tk = it * 8 + (lane >> 3), c8 = lane & 7;    // token of the wave, 16-byte chunk
+    const frag val = *(const frag*)(ob + tk * 128 + ((c8 ^ (tk & 7)) << 4));
+    const int s = 32 * half + tk;
+    if (fr < BT && s < NB) *(frag*)((T*)L.O + ((int64_t)s * BT + fr) * I + h * 64 + 8 * c8) = val;
+  }
+}
+
+}  // namespace
+
+bool band_attn_supported(int dtype, int NB, int heads, int dh, int D) {
+  return dtype != DT_F32 && dh == 64 && NB >= 1 && NB <= 64 && heads >= 1 && D % 32 == 0 && D <= 1024;
+}
+
+hipError_t launch_band_attn(const BandLaunch& L, hipStream_t stream) {
+  if (!band_attn_supported(L.dtype, L.NB, L.heads, 64, L.D) || L.BT < 1) return hipErrorInvalidValue;
+  const int groups = (L.BT + 3) / 4;
+  const dim3 grid((unsigned)(groups * L.heads)), block(512);
+  if (L.dtype == DT_F16) {
+    hipError_t e = hipFuncSetAttribute((const void*)band_attn_kernel<f16>, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(band_attn_kernel<f16>, grid, block, kLds, stream, L);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)band_attn_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(band_attn_kernel<bf16>, grid, block, kLds, stream, L);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mbr

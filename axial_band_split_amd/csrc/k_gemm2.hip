@@ -80,6 +80,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
   constexpr int NW = C::WM * C::WN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / C::WN, wn = w % C::WN;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform: LDS targets stay scalar
   const int M = L.M;
   GemmGroup g;
   int m0, n0;
@@ -105,24 +106,24 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
   // and B rows (rows past the end read the last row), into wave-uniform LDS targets
   const int64_t lda_b = (int64_t)g.lda * 2, ldb_b = (int64_t)g.ldb * 2;
   const int arows = min(BM, M - m0), brows = max(1, min(BN, g.N - n0));
-  const __amdgpu_buffer_rsrc_t ars =
-      buffer_rsrc((const char*)L.A + (g.a_off0 + g.a_offb * (int64_t)M) * 2 + (int64_t)m0 * lda_b, (uint32_t)(arows * lda_b));
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc_uniform(
+      (const char*)L.A + (g.a_off0 + g.a_offb * (int64_t)M) * 2 + (int64_t)m0 * lda_b, (uint32_t)(arows * lda_b));
   const __amdgpu_buffer_rsrc_t brs =
-      buffer_rsrc((const char*)L.B + g.b_off * 2 + (int64_t)n0 * ldb_b, (uint32_t)(brows * ldb_b));
+      buffer_rsrc_uniform((const char*)L.B + g.b_off * 2 + (int64_t)n0 * ldb_b, (uint32_t)(brows * ldb_b));
   int voff[C::LOADS], dst[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LD; ++j) {
     const int row = (j * NW + w) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(row);
     voff[j] = (int)(min(row, arows - 1) * lda_b) + c * 16;
-    dst[j] = (j * NW + w) * 1024;
+    dst[j] = (j * NW + wu) * 1024;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LD; ++j) {
     const int row = (j * NW + w) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(row);
     voff[C::A_LD + j] = (int)(min(row, brows - 1) * ldb_b) + c * 16;
-    dst[C::A_LD + j] = C::A_BYTES + (j * NW + w) * 1024;
+    dst[C::A_LD + j] = C::A_BYTES + (j * NW + wu) * 1024;
   }
   // K order rotated by the column tile: the tiles that share an A panel (same m0) run at the same
   // time, and in plain order all of them would ask for each K chunk at once and every one would

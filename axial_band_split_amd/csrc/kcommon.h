@@ -89,6 +89,14 @@ constexpr float kNormEps = 1e-12f;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// The same over a base and size the caller knows to be wave-uniform but the compiler may not (values
+// read from memory): taken from the first lane, so the descriptor lives in scalar registers and
+// every load through it is one instruction (a descriptor in vector registers costs a loop per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return buffer_rsrc((const void*)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
 // 16 bytes per lane from buffer offset voff (per lane) + soff (uniform) into LDS at
 // lds_wave_base + 16 * lane.  The buffer form of the LDS load and not the global one: with a
 // FLAT-encoded load to LDS in flight the compiler must assume LDS reads complete out of order and

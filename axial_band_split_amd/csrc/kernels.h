@@ -153,6 +153,24 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t stream);
 hipError_t launch_attention_time2(const AttnLaunch& L, hipStream_t stream);
 bool attention_time2_supported(int dqk, int dv);
 
+// The band axis' q, k, v projection, rotary, attention over the bands of each frame and the gated
+// output of one Transformer in one kernel (16-bit operands, dh = 64): O[token][h*64 + d].
+struct BandLaunch {
+  int dtype;
+  const void* XH;           // [NB * BT][D] x^ (normalised unless rowss is given)
+  const void* W;            // [3*H*64 + 64][D] W_qkv with the gate rows after q, k, v (the 16-bit repack)
+  const float* gate_bias;   // [H]
+  const float* cos;         // [64][32] rotary tables of the band positions
+  const float* sin;
+  const float* rowss;       // optional row statistics of x^ (row scale rs_mul / |x|)
+  float rs_mul;
+  float q_mul;              // log2 e: scores in log2 units
+  void* O;                  // [NB * BT][H*64] gated attention output
+  int32_t NB, BT, heads, D;
+};
+bool band_attn_supported(int dtype, int NB, int heads, int dh, int D);
+hipError_t launch_band_attn(const BandLaunch& L, hipStream_t stream);
+
 // y = gelu(x) elementwise with the device GELU of the feed-forward epilogues (test surface).
 hipError_t launch_gelu(const float* x, float* y, int n, hipStream_t stream);
 

@@ -124,6 +124,7 @@ struct mbr_core {
   int v_embed = 0, v_qkv = 0, v_out = 0, v_ffn1 = 0, v_ffn2 = 0, v_mask = 0, v_glu = 0;
   int glu_blk = 16;                   // value / gate pairing block of the last mask layer
   bool use_block = false;             // 16-bit path with the fused post-attention kernel
+  bool use_band = false;              // 16-bit path: band axis' projection and attention in one kernel
   int kpad_total = 0, kpad_max = 0;
   // device memory
   char* wdev = nullptr;               // dtype weights
@@ -473,7 +474,7 @@ int alloc_workspace(mbr_core* c) {
     return o;
   };
   const size_t attn_t = (size_t)c->NB * c->Bmax * c->H * c->Tp * c->DH * esz;
-  const size_t attn_b = BT * c->H * 64 * c->DH * esz;
+  const size_t attn_b = c->use_band ? 0 : BT * c->H * 64 * c->DH * esz;   // unused by the fused band kernel
   size_t oX = place(NT * c->D * 4), oXH = place(NT * c->D * esz), oG = place(NT * c->H * 4),
          oU = place(BT * c->kpad_total * esz), oqt = place(attn_t), okt = place(attn_t), ovt = place(attn_t),
          oqb = place(attn_b), okb = place(attn_b), ovb = place(attn_b), oO = place(NT * c->I * esz),
@@ -586,6 +587,28 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   for (int t = 0; t < ntr; ++t) {
     const TransformerW& tw = c->tw[t];
     const int axis = t & 1;
+    if (axis == 1 && c->use_band) {
+      // the band axis: q, k, v of one head for four frames, rotary, attention over the bands and
+      // the gate, in one kernel (q, k, v stay on the chip)
+      BandLaunch bd{};
+      bd.dtype = dt;
+      bd.XH = c->XH;
+      bd.W = wptr(tw.wqkv);
+      bd.gate_bias = c->fdev + tw.bg;
+      bd.cos = c->cos_b;
+      bd.sin = c->sin_b;
+      if (!c->use_block) {   // XH carries the previous output, not yet normalised
+        bd.rowss = c->ssB;
+        bd.rs_mul = sqrtD;
+      }
+      bd.q_mul = 1.4426950408889634f;
+      bd.O = c->O;
+      bd.NB = c->NB;
+      bd.BT = BT;
+      bd.heads = c->H;
+      bd.D = c->D;
+      LAUNCH(MBR_K_BAND_ATTN, launch_band_attn(bd, s));
+    } else {
     // q, k, v with rotary, scattered per axis
     GemmLaunch gq{};
     gq.dtype = dt;
@@ -641,6 +664,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     al.scale_log2 = fused ? 1.0f : 1.4426950408889634f;
     LAUNCH(axis ? MBR_K_ATTN_BAND : MBR_K_ATTN_TIME,
            (axis == 0 && dt != MBR_F32) ? launch_attention_time2(al, s) : launch_attention(al, s));
+    }
 
     const bool last = t == ntr - 1;
     if (c->use_block) {
@@ -909,6 +933,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
   c->v_glu = 2;
   c->v_embed = 4;
   c->use_block = block_supported(cfg->dtype, c->D, c->I, c->FF);
+  c->use_band = band_attn_supported(cfg->dtype, c->NB, c->H, c->DH, c->D);
   c->kpad.resize(c->NB);
   c->kcol.resize(c->NB);
   c->wp.resize(c->NB);

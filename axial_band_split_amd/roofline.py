@@ -60,8 +60,9 @@ KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E", "qkv": r"gemm2_kernelIDF16b
               "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
               "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
               "norm": r"norm", "gather": r"gather", "average": r"average",
-              "block": r"block2?_kernel|block_reduce_kernel"}
-MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block")
+              "block": r"block_kernel|block_reduce_kernel", "band_attn": r"band_attn_kernel"}
+MFMA_KINDS = ("embed", "qkv", "attn_time", "out_proj", "ffn1", "ffn2", "mask_hidden", "mask_glu", "block",
+              "band_attn")
 HBM_KINDS = ("gather", "average", "attn_band", "norm")
 
 
@@ -84,6 +85,8 @@ def flops_per_launch(s: Shape) -> Dict[str, float]:
         "mask_glu": 2.0 * s.stems * BT * s.MH * 2 * s.total_width,
         # out-projection + feed-forward of one Transformer in one kernel (16-bit path)
         "block": 2.0 * N * I * D + 4.0 * N * D * s.FF,
+        # the band axis' q, k, v projection and attention in one kernel (16-bit path)
+        "band_attn": 2.0 * N * D * 3 * I + 2.0 * 2.0 * BT * H * s.NB * s.NB * s.dh,
     }
 
 

@@ -203,7 +203,9 @@ enum {
   MBR_K_AVERAGE = 11,    /* inverse-index mask average                                   */
   MBR_K_BLOCK = 12,      /* 16-bit path: out-projection, residual, feed-forward and both
                             norms of a Transformer in one kernel (replaces 6, 7, 8)      */
-  MBR_K_COUNT = 13
+  MBR_K_BAND_ATTN = 13,  /* 16-bit path: the band axis' q/k/v projection, rotary, attention
+                            and gates in one kernel (replaces 3 and 5 on that axis)      */
+  MBR_K_COUNT = 14
 };
 /*
  * The same forward as mbr_core_forward, with a HIP event pair recorded on `stream` around every
