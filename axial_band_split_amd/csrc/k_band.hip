@@ -1,5 +1,5 @@
 // The band-axis attention of a Transformer in one kernel (fp16 / bf16): the q, k, v projection of
-// one head for the bands of four frames, the attention over the bands of each frame, and the gated
+// one head for the bands of a few frames, the attention over the bands of each frame, and the gated
 // output, with q, k and v never leaving the compute unit.
 //
 // ([P1] "The two transformers are not the same shape": the band Transformer runs one sequence per
@@ -8,8 +8,9 @@
 // The scale 1/sqrt(dh) is folded into W_q at create; q is multiplied by log2 e here so the
 // exponentials are base 2.)
 //
-// Workgroup = (4 frames, head h), 8 waves.  The 4 x 64 band slots of the frames (bands >= NB are
-// padding rows, read as a valid row and masked as keys) are the rows of a 256 x 192 x D product
+// Workgroup = (FR frames, head h), two waves per frame (FR = 2).  The FR x 64 band slots of the
+// frames (bands >= NB are padding rows, read as a valid row and masked as keys) are the rows of a
+// 64 FR x 192 x D product
 // against the head's rows of W_qkv ([q_h | k_h | v_h]); K goes through a 3-stage LDS ring by 16-byte
 // direct loads, as in the GEMM.  Wave (f, r) owns the 32 band slots 32r .. 32r+31 of frame f and all
 // 192 columns (six 32 x 32 tiles on v_mfma_f32_32x32x16):
@@ -54,16 +55,28 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 constexpr float kNegBig = -1e30f;
 
-constexpr int kRows = 256;               // 4 frames x 64 band slots
-constexpr int kCols = 192;               // [q_h | k_h | v_h], dh = 64
-constexpr int kStage = (kRows + kCols) * 64;   // one K step of 32: 28 KB
-constexpr int kNS = 3;
-constexpr int kExch = 8 * 8192;          // per wave: its keys' 4 k and 4 v fragments
-constexpr int kOut = 8 * 4096;           // per wave: 32 tokens x 64 outputs, 16-bit
-constexpr int kLds = (kNS * kStage > kExch + kOut ? kNS * kStage : kExch + kOut);
+// FR frames per workgroup, two waves per frame
+template <int FR>
+struct BandCfg {
+  static constexpr int kRows = 64 * FR;                  // FR frames x 64 band slots
+  static constexpr int kCols = 192;                      // [q_h | k_h | v_h], dh = 64
+  static constexpr int kWaves = 2 * FR, kThreads = 64 * kWaves;
+  static constexpr int kStage = (kRows + kCols) * 64;    // one K step of 32
+  static constexpr int kNS = 3;
+  static constexpr int kExch = kWaves * 8192;            // per wave: its keys' 4 k and 4 v fragments
+  static constexpr int kOut = kWaves * 4096;             // per wave: 32 tokens x 64 outputs, 16-bit
+  static constexpr int kLds = (kNS * kStage > kExch + kOut ? kNS * kStage : kExch + kOut);
+  static constexpr int kALoads = kRows * 4 / kThreads;   // 16-byte A loads per thread per stage (2)
+  static constexpr int kBChunks = kCols * 4;             // 768
+  static constexpr int kBLoads = (kBChunks + kThreads - 1) / kThreads;
+  static_assert(kALoads * kThreads == kRows * 4, "A loads");
+};
 
-template <typename T>
-__global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
+template <typename T, int FR>
+__global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch L) {
+  using C = BandCfg<FR>;
+  constexpr int kRows = C::kRows, kCols = C::kCols, kStage = C::kStage, kNS = C::kNS, kExch = C::kExch,
+                NT = C::kThreads, NW = C::kWaves;
   using frag = typename Frag<T>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ __attribute__((aligned(16))) float wg[1024];   // the head's gate weights (D <= 1024)
@@ -78,9 +91,9 @@ __global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
   const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int logical = xcd * per + min(xcd, rem) + slot;
-  const int h = logical % L.heads, f0 = (logical / L.heads) * 4;
+  const int h = logical % L.heads, f0 = (logical / L.heads) * FR;
 
-  for (int i = tid; i < D; i += 512) wg[i] = tof<T>(((const T*)L.W)[(size_t)(3 * I + h) * D + i]);
+  for (int i = tid; i < D; i += NT) wg[i] = tof<T>(((const T*)L.W)[(size_t)(3 * I + h) * D + i]);
   __syncthreads();
 
   // ---- loader.  A row rho: frame f0 + rho/64, band slot rho%64 -> token slot*BT + frame (padding
@@ -88,28 +101,29 @@ __global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
   const int64_t rowb = (int64_t)D * 2;
   const __amdgpu_buffer_rsrc_t ars = buffer_rsrc_uniform(L.XH, (uint32_t)((int64_t)NB * BT * rowb));
   const __amdgpu_buffer_rsrc_t brs = buffer_rsrc_uniform(L.W, (uint32_t)((int64_t)(3 * I + 64) * rowb));
-  int voff[4];
-  bool bload2 = false;
+  int voff[C::kALoads + C::kBLoads];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {            // A: 1024 chunks
-    const int c = j * 512 + tid, row = c >> 2, pc = c & 3;
+  for (int j = 0; j < C::kALoads; ++j) {   // A: 4 chunks per row
+    const int c = j * NT + tid, row = c >> 2, pc = c & 3;
     const int f = min(f0 + (row >> 6), BT - 1), s = min(row & 63, NB - 1);
     voff[j] = (int)(((int64_t)s * BT + f) * rowb) + ((pc ^ swz(row)) << 4);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {            // B: 768 chunks (the second round: waves 0..3)
-    const int c = j * 512 + tid, row = min(c >> 2, kCols - 1), pc = c & 3;
+  for (int j = 0; j < C::kBLoads; ++j) {   // B: 768 chunks (a partial last round covers the first waves)
+    const int c = j * NT + tid, row = min(c >> 2, kCols - 1), pc = c & 3;
     const int wrow = (row >> 6) * I + h * 64 + (row & 63);
-    voff[2 + j] = (int)(wrow * rowb) + ((pc ^ swz(row)) << 4);
+    voff[C::kALoads + j] = (int)(wrow * rowb) + ((pc ^ swz(row)) << 4);
   }
-  bload2 = wu < 4;
+  // loads of this wave per stage (the partial last B round only for waves below its end)
+  const bool blast = ((C::kBLoads - 1) * NT + wu * 64) < C::kBChunks;
   auto issue = [&](int ks) {
     char* base = smem + (ks % kNS) * kStage;
     const int ko = ks * 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) buffer_dma16(ars, voff[j], ko, base + (j * 8 + wu) * 1024);
-    buffer_dma16(brs, voff[2], ko, base + kRows * 64 + wu * 1024);
-    if (bload2) buffer_dma16(brs, voff[3], ko, base + kRows * 64 + (8 + wu) * 1024);
+    for (int j = 0; j < C::kALoads; ++j) buffer_dma16(ars, voff[j], ko, base + (j * NW + wu) * 1024);
+#pragma unroll
+    for (int j = 0; j < C::kBLoads; ++j)
+      if (j < C::kBLoads - 1 || blast) buffer_dma16(brs, voff[C::kALoads + j], ko, base + kRows * 64 + (j * NW + wu) * 1024);
   };
 
   // ---- the 256 x 192 product; this wave: rows 64 fl + 32 half + (0..31), all six column tiles.
@@ -125,9 +139,9 @@ __global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
   issue(0);
   if (nk > 1) issue(1);
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) {                      // at most the next stage's loads outstanding (3 or 4)
-      if (bload2) wait_vm<4>();
-      else wait_vm<3>();
+    if (ks + 1 < nk) {                      // at most the next stage's loads outstanding
+      if (blast) wait_vm<C::kALoads + C::kBLoads>();
+      else wait_vm<C::kALoads + C::kBLoads - 1>();
     } else {
       wait_vm<0>();
     }
@@ -278,6 +292,7 @@ __global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
   // ---- gated output: stage [token][64] 16-bit rows per wave, then 16-byte stores of whole rows
   const float scale = gate / lsum;
   char* ob = smem + kExch + wu * 4096;
+  static_assert(NW == 2 * FR, "two waves per frame");
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -301,24 +316,29 @@ __global__ __launch_bounds__(512, 1) void band_attn_kernel(BandLaunch L) {
 
 }  // namespace
 
+namespace {
+template <typename T, int FR>
+hipError_t launch_fr(const BandLaunch& L, hipStream_t stream) {
+  using C = BandCfg<FR>;
+  const int groups = (L.BT + FR - 1) / FR;
+  hipError_t e = hipFuncSetAttribute((const void*)band_attn_kernel<T, FR>, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((band_attn_kernel<T, FR>), dim3((unsigned)(groups * L.heads)), dim3(C::kThreads), C::kLds, stream, L);
+  return hipGetLastError();
+}
+}  // namespace
+
 bool band_attn_supported(int dtype, int NB, int heads, int dh, int D) {
   return dtype != DT_F32 && dh == 64 && NB >= 1 && NB <= 64 && heads >= 1 && D % 32 == 0 && D <= 1024;
 }
 
 hipError_t launch_band_attn(const BandLaunch& L, hipStream_t stream) {
   if (!band_attn_supported(L.dtype, L.NB, L.heads, 64, L.D) || L.BT < 1) return hipErrorInvalidValue;
-  const int groups = (L.BT + 3) / 4;
-  const dim3 grid((unsigned)(groups * L.heads)), block(512);
-  if (L.dtype == DT_F16) {
-    hipError_t e = hipFuncSetAttribute((const void*)band_attn_kernel<f16>, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(band_attn_kernel<f16>, grid, block, kLds, stream, L);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void*)band_attn_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(band_attn_kernel<bf16>, grid, block, kLds, stream, L);
-  }
-  return hipGetLastError();
+  // two frames (four waves) per workgroup, two workgroups per compute unit: one's projection
+  // overlaps the other's attention (0.90 ms per forward at 1100 frames against 0.97 for four frames
+  // per workgroup, one per compute unit)
+  if (L.dtype == DT_F16) return launch_fr<f16, 2>(L, stream);
+  return launch_fr<bf16, 2>(L, stream);
 }
 
 }  // namespace mbr

@@ -515,3 +515,22 @@ def test_large_batches_and_long_chunks(frames, batch, picks, oracle_pick):
         assert err <= TOL[w.dtype]
         check_parts("large", yb[i:i + 1].cpu().numpy(), ref, w, TOL[w.dtype])
     core.close()
+
+
+@pytest.mark.parametrize("dtype,bands,frames,batch", [(synth.F16, 24, 45, 3), (synth.BF16, 64, 7, 2)])
+def test_fused_band_axis_at_other_band_counts(dtype, bands, frames, batch):
+    """The band axis' fused projection and attention (dim 384, 8 x 64 heads) with 24 mel bands (40 of
+    the 64 key slots of a frame masked) and with 64 (none masked), over frame counts whose last
+    group of four frames is partly empty (135 and 14 frames in all)."""
+    w = synth.WORKLOADS["t256_fp16"].replace(num_bands=bands, frames=frames, batch=batch, depth=1, dtype=dtype)
+    say(f"[band] {bands} bands, T={frames}, B={batch}, {synth.DTYPE_NAMES[dtype]}")
+    cfg, ws = build(w)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    ref = M.forward(x, ocfg(w), ws)
+    err = rel_l2(y, ref)
+    say(f"[band] rel L2 = {err:.3e}")
+    assert np.isfinite(y).all() and err <= TOL[dtype]
+    check_parts("band", y, ref, w, TOL[dtype], frame_block=16)
