@@ -8,6 +8,7 @@
     python -m axial_band_split_amd.profiling sweep <bench line .json> ... <out.md> --command "<cmd>"
     python -m axial_band_split_amd.profiling roofline <kernel_stats.csv> <fetch.csv> <write.csv> <cal_fetch.csv>
                                                       <cal_write.csv> <sq.csv> <workload> <out.md> --command "<cmd>"
+    python -m axial_band_split_amd.profiling waves <pass1.csv> <pass2.csv> <workload> <out.md> --command "<cmd>"
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into bytes per launch,
 each scaled by what the same counter reads for a plain device copy of known size (the calibration
@@ -206,6 +207,41 @@ def roofline_md(stats_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, s
     return "\n".join(rows) + "\n"
 
 
+def waves_md(pass1_csv, pass2_csv, workload, command) -> str:
+    """Where each kernel class's waves spend their cycles, from two counter passes over the same
+    program: fractions of SQ_WAVE_CYCLES (busy, waiting on a counter, waiting to issue, issuing any /
+    vector-and-matrix / LDS instructions, waiting on LDS), LDS bank-conflict cycles per LDS
+    instruction, vector instructions per matrix instruction, and the matrix-core busy fraction."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    from axial_band_split_amd import roofline as R
+    rows = ["# Where the waves spend their cycles (" + workload + ")", "", f"Command: `{command}`", "",
+            "Fractions of SQ_WAVE_CYCLES per kernel class (mean per dispatch, summed over the class's kernels); "
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs).", "",
+            "| kernel class | busy | wait (any) | wait for issue | issuing any | issuing VALU+MFMA | issuing LDS | "
+            "waiting on LDS | LDS bank-conflict cycles / LDS instr | VALU / MFMA instr | MFMA busy |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for kind, rx in R.KIND_REGEX.items():
+        try:
+            wc = _one(pass1_csv, "SQ_WAVE_CYCLES", rx)
+        except SystemExit:
+            continue
+        g1 = lambda c: _one(pass1_csv, c, rx)
+        g2 = lambda c: _one(pass2_csv, c, rx)
+        try:
+            mfma = g2("SQ_INSTS_MFMA")
+            ratio = g2("SQ_INSTS_VALU") / mfma if mfma else float("nan")
+            busy = g2("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * g2("GRBM_GUI_ACTIVE") / N_XCD)
+            act_any, act_valu = g2("SQ_ACTIVE_INST_ANY") / wc, g2("SQ_ACTIVE_INST_VALU") / wc
+        except SystemExit:
+            ratio = busy = act_any = act_valu = float("nan")
+        lds = g1("SQ_INSTS_LDS")
+        conf = g1("SQ_LDS_BANK_CONFLICT") / lds if lds else 0.0
+        rows.append(f"| {kind} | {g1('SQ_BUSY_CYCLES') / wc:.2f} | {g1('SQ_WAIT_ANY') / wc:.2f} | "
+                    f"{g1('SQ_WAIT_INST_ANY') / wc:.2f} | {act_any:.2f} | {act_valu:.2f} | {g1('SQ_ACTIVE_INST_LDS') / wc:.2f} | "
+                    f"{g1('SQ_WAIT_INST_LDS') / wc:.2f} | {conf:.2f} | {ratio:.1f} | {100 * busy:.0f}% |")
+    return "\n".join(rows) + "\n"
+
+
 def sweep_md(paths, command) -> str:
     """One row per bench line: the workload's shape, throughput and the per-kernel device time."""
     recs = [json.loads(open(p).read().strip().splitlines()[-1]) for p in paths]
@@ -250,6 +286,10 @@ def main(argv=None):
     e = sub.add_parser("sweep")
     e.add_argument("paths", nargs="+")
     e.add_argument("--command", required=True)
+    f = sub.add_parser("waves")
+    for n in ("pass1", "pass2", "workload", "out"):
+        f.add_argument(n)
+    f.add_argument("--command", required=True)
     d = sub.add_parser("roofline")
     for n in ("stats", "fetch", "write", "cal_fetch", "cal_write", "sq", "workload", "out"):
         d.add_argument(n)
@@ -260,6 +300,9 @@ def main(argv=None):
         return 0
     if args.what == "sweep":
         open(args.paths[-1], "w").write(sweep_md(args.paths[:-1], args.command))
+        return 0
+    if args.what == "waves":
+        open(args.out, "w").write(waves_md(args.pass1, args.pass2, args.workload, args.command))
         return 0
     if args.what == "roofline":
         open(args.out, "w").write(roofline_md(args.stats, args.fetch, args.write, args.cal_fetch, args.cal_write,
