@@ -8,8 +8,7 @@
 //
 // ([P1] "Per Attention layer", "The forward chain"; [P5] export-roformer.py classes Attn, FF and
 // Block: the residual adds, the erf GELU feed-forward and the RMSNorm with its 1e-12 clamp.  The
-// erf of the GELU is evaluated to 5e-4 here, below the 16-bit rounding of the hidden layer; see
-// gelu_as27.)
+// GELU is evaluated to 1.3e-4 here, below the 16-bit rounding of the hidden layer; see gelu2_hidden.)
 //
 // Tokens are the N side of every product: a wave owns 32 tokens and keeps, for all of them,
 // the whole residual row in its accumulators (D/32 tiles of 32 x 32 on v_mfma_f32_32x32x16; lane
@@ -107,23 +106,22 @@ __device__ __forceinline__ void pipelined(RD rd, MM mm, HK hook) {
   }, std::make_integer_sequence<int, G>{});
 }
 
-// GELU of the hidden layer with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.27: erf(z) = 1 - d^-4, d = 1 + a1 z + a2 z^2 + a3 z^3 + a4 z^4, |error| <= 5e-4, with
-// z = |x| / sqrt(2) folded into the coefficients (a_k / 2^(k/2)).  GELU(x) = x (1 + erf) / 2, i.e.
-// x - x d^-4 / 2 for x >= 0 and x d^-4 / 2 below: eleven vector instructions against the fifteen of
-// the 7.1.26 form, whose 1.5e-7 is far below what this path keeps (the result is rounded to 16 bits,
-// a relative step of 4.9e-4 in fp16); the GELU error stays under 7e-4 absolute, 2.3e-4 relative for
-// |x| >= 1.  The vector work per product is what bounds this kernel's issue rate.
-__device__ __forceinline__ float gelu_as27(float x) {
-  const float ax = fabsf(x);
-  float d = fmaf(0.0195270f, ax, 0.000343654f);
-  d = fmaf(d, ax, 0.1151945f);
-  d = fmaf(d, ax, 0.1968536f);
-  d = fmaf(d, ax, 1.0f);
-  d = d * d;
-  const float t = 0.5f * __builtin_amdgcn_rcpf(d * d);   // (1 - erf) / 2
-  const float y = x * t;
-  return x >= 0.f ? x - y : y;
+// Twice the GELU of the hidden layer (the W_2 columns of the weight stream carry the factor 1/2,
+// which is exact): 2 x Phi(x) = x + |x| (1 - 2 Q(|x|)), Q the upper tail of the standard normal
+// distribution, with 2 Q(a) = 2^p(a) for a cubic p without constant term (so 2 Q(0) = 1 exactly); its
+// three coefficients are a minimax fit of the weighted error max(a, 1) |2^(p(a) - 1) - Q(a)| over
+// [0, 10] (gelu_tail_fit.py beside this file).  All three are negative, so p falls for every a >= 0
+// and the tail goes to zero.  The GELU is within 1.3e-4 absolute and 1.3e-4 |x| of the erf GELU
+// everywhere, below the 16-bit rounding of the hidden layer (a relative step of 4.9e-4 in fp16); for
+// large negative x the sum cancels to within 1e-7 absolute.  Four vector instructions, one exp2 and
+// the add that also rounds to 16 bits per value: the vector work per product is what bounds this
+// kernel's issue rate.
+__device__ __forceinline__ float gelu2_hidden(float x) {
+  const float a = fabsf(x);
+  float p = fmaf(-0.030005693f, a, -0.48125008f);
+  p = fmaf(p, a, -1.1454322f);
+  p *= a;
+  return fmaf(a, 1.0f - __builtin_amdgcn_exp2f(p), x);
 }
 
 template <typename T, int D_, int I_, int NS_, int GS_>
@@ -333,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
       if constexpr (dog) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (G == 0 || 1 + v * G / 16 == g) (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu_as27(o0[v]));
+          if (G == 0 || 1 + v * G / 16 == g) (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu2_hidden(o0[v]));
       }
     };
     if constexpr (NA + NB == 0) {

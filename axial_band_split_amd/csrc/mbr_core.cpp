@@ -316,7 +316,8 @@ int setup_tables_and_groups(mbr_core* c) {
 //   stages 0 .. I/64-1: out-projection, K step ks of 4, tile t of D/32 (rows 32t..): W_out[row][k]
 //   stage I/64 + c:     W_1 rows of hidden chunk c (K steps s of D/16) with the columns permuted to
 //                       the accumulator's row order, then W_2 columns of chunk c-2 (tile t, step s2)
-//                       permuted to the order the hidden tile holds its rows.
+//                       permuted to the order the hidden tile holds its rows, times 1/2 (the kernel's
+//                       hidden layer holds twice the GELU).
 // The accumulator of a 32 x 32 product holds in lane l rows 8(v/4) + 4(l/32) + v%4 (v = 0..15); read
 // as a B operand, K step s of a 32-row tile takes v = 8(s%2) + e, i.e. row
 // perm(s, h, e) = 32(s/2) + 8(2(s%2) + e/4) + 4h + e%4 for lane half h and element e.
@@ -347,7 +348,7 @@ std::vector<double> block_stream(int D, int I, int FF, const std::vector<double>
           for (int l = 0; l < 64; ++l)
             for (int e = 0; e < 8; ++e)
               out[base + (size_t)(D / 16) * 512 + ((size_t)(2 * t + s2) * 64 + l) * 8 + e] =
-                  w2[(size_t)(32 * t + l % 32) * FF + 32 * (c - 2) + perm(s2, l / 32, e)];
+                  0.5 * w2[(size_t)(32 * t + l % 32) * FF + 32 * (c - 2) + perm(s2, l / 32, e)];
   }
   return out;
 }
