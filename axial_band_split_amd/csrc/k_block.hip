@@ -10,22 +10,23 @@
 // Block: the residual adds, the erf GELU feed-forward and the RMSNorm with its 1e-12 clamp.  The
 // GELU is evaluated to 1.3e-4 here, below the 16-bit rounding of the hidden layer; see gelu2_hidden.)
 //
-// Tokens are the N side of every product: a wave owns 32 tokens and keeps, for all of them,
-// the whole residual row in its accumulators (D/32 tiles of 32 x 32 on v_mfma_f32_32x32x16; lane
-// l holds token l % 32 and rows 8(v/4) + 4(l/32) + v%4 of each tile), so the norms are lane sums
-// and one exchange with lane l ^ 32, and neither x1 nor the FF-wide hidden layer ever leaves the
-// registers:
+// Tokens are the N side of every product: a wave owns 16 tokens and keeps, for all of them,
+// the whole residual row in its accumulators (D/16 tiles of 16 x 16 on v_mfma_f32_16x16x32; lane
+// l holds token l % 16 and rows 4(l/16) + v, v = 0..3, of each tile), so the norms are lane sums
+// and two exchanges (lanes l ^ 16, l ^ 32), and neither x1 nor the FF-wide hidden layer ever leaves
+// the registers:
 //   * x1 feeds the first feed-forward product directly as its B operand: the columns of W_1 are
-//     permuted once (at create) into the order in which the accumulator holds the rows;
-//   * the hidden layer is produced 32 features at a time (a 32 x 32 tile per wave), goes through
+//     permuted once (at create) into the order in which the accumulators hold the rows;
+//   * the hidden layer is produced 32 features at a time (two 16 x 16 tiles per wave), goes through
 //     GELU in registers and is the B operand of the second product, whose K order is permuted the
 //     same way;
 //   * the second product accumulates onto x1 + b_2, so the residual add is free.
 // The weights are one stream of equal stages (out-projection K steps of 64, then per 32 hidden
-// features the W_1 rows of chunk c and the W_2 columns of chunk c-1), laid out at create in
+// features the W_1 rows of chunk c and the W_2 columns of chunk c-2), laid out at create in
 // exactly the order the lanes read them: a stage is copied into LDS by 16-byte direct loads and
-// every fragment read is one conflict-free 16-byte LDS read per lane.  Four waves (128 tokens)
-// share each stage; NS stages are in flight.
+// every fragment read is one conflict-free 16-byte LDS read per lane.  Eight waves (128 tokens, two
+// waves per SIMD, so one wave's products cover the other's LDS reads and vector work) share each
+// stage; NS stages are in flight.
 //
 // Whole device passes (one 128-token block per compute unit) run every hidden chunk in
 // each block.  The tokens left after them would leave most compute units idle for a full block's
@@ -41,14 +42,12 @@ namespace mbr {
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ void mma32(f32x16& c, const f16x8& a, const f16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void mma32(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+#ifndef BLK_GS
+#define BLK_GS 3
+#endif
+#ifndef BLK_VPM
+#define BLK_VPM 4
+#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -124,44 +123,47 @@ __device__ __forceinline__ float gelu2_hidden(float x) {
   return fmaf(a, 1.0f - __builtin_amdgcn_exp2f(p), x);
 }
 
-template <typename T, int D_, int I_, int NS_, int GS_>
+template <typename T, int D_, int I_, int NS_, int GS_, int VPM_>
 struct BlockCfg {
-  static constexpr int D = D_, I = I_, NS = NS_, GS = GS_;   // GS: fragments per read group
-  static constexpr int DT = D / 32;                 // accumulator tiles per wave
+  // GS: fragments per read group; VPM: vector instructions placed after each feed-forward product
+  static constexpr int D = D_, I = I_, NS = NS_, GS = GS_, VPM = VPM_;
+  static constexpr int WAVES = 8, THREADS = 64 * WAVES;
+  static constexpr int DT = D / 16;                 // accumulator tiles per wave
   static constexpr int FF = 4 * D;
   static constexpr int NCH = FF / 32;               // hidden chunks of 32 features
   static constexpr int KO = I / 64;                 // out-projection stages (K = 64 each)
   static constexpr int NST = KO + NCH + 2;          // stages in the stream
-  // stage bytes: D/8 fragments of 1 KB (out-projection: 4 K steps x D/32 tiles; feed-forward:
-  // D/16 K steps of W_1 + 2 K steps x D/32 tiles of W_2)
+  // stage bytes: D/8 fragments of 1 KB (out-projection: 2 K steps x D/16 tiles; feed-forward:
+  // 2 W_1 tiles x D/32 K steps, then D/16 tiles of W_2)
   static constexpr int SB = D * 128;
-  static constexpr int R = SB / 4096;               // 16-byte loads per thread per stage
+  static constexpr int R = SB / (16 * THREADS);     // 16-byte loads per thread per stage
   static constexpr int LDS = NS * SB;               // the ring (b_1 is a static LDS array)
+  static_assert(R * 16 * THREADS == SB, "stage split");
 };
 
 template <typename T, typename C, bool ALL_CHUNKS>
-__global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
+__global__ __launch_bounds__(C::THREADS, 2) void block_kernel(BlockLaunch L) {
   typedef typename Frag<T>::type frag;
   constexpr int D = C::D, I = C::I, NS = C::NS, DT = C::DT, NCH = C::NCH, KO = C::KO, NST = C::NST,
-                SB = C::SB, R = C::R, FF = C::FF, GS = C::GS;
+                SB = C::SB, R = C::R, FF = C::FF, GS = C::GS, TH = C::THREADS;
   auto none = [](auto) {};
   extern __shared__ __attribute__((aligned(16))) char smem[];   // the weight ring
   __shared__ __attribute__((aligned(16))) float b1s[FF];        // b_1, a separate LDS object
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
-  // block = (token group, chunk group q); a wave owns 32 tokens of the group's 128 and runs the
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qd = lane >> 4;
+  // block = (token group, chunk group q); a wave owns 16 tokens of the group's 128 and runs the
   // hidden chunks [c0, c0 + n) (n even, at least 2).  With ALL_CHUNKS (the whole passes) the
   // block runs every chunk and the trip counts are compile-time constants.
   const int groups = ALL_CHUNKS ? 1 : L.groups;
   const int q = ALL_CHUNKS ? 0 : blockIdx.x % groups;
   const int n = ALL_CHUNKS ? NCH : NCH / groups, c0 = q * n;
-  const int64_t token = (ALL_CHUNKS ? 0 : L.tok0) + (int64_t)(blockIdx.x / groups) * 128 + w * 32 + (lane & 31);
+  const int64_t token = (ALL_CHUNKS ? 0 : L.tok0) + (int64_t)(blockIdx.x / groups) * 128 + w * 16 + (lane & 15);
   const bool valid = token < L.tokens;
   // lanes past the last token read the last token's row and store nothing (a token's lanes only
   // ever combine with each other)
   const int64_t tload = valid ? token : (int64_t)L.tokens - 1;
 
-  for (int i = tid; i < FF; i += 256) b1s[i] = L.b1[i];
+  for (int i = tid; i < FF; i += TH) b1s[i] = L.b1[i];
   __syncthreads();
 
   const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform: LDS bases stay scalar
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     const int g = (i < KO ? i : i + c0) * SB;
     char* l = smem + (i % NS) * SB + wu * 1024;
 #pragma unroll
-    for (int r = 0; r < R; ++r) buffer_dma16(srs, tid * 16, g + r * 4096, l + r * 4096);
+    for (int r = 0; r < R; ++r) buffer_dma16(srs, tid * 16, g + r * 16 * TH, l + r * 16 * TH);
   };
   // step i's stage is complete once at most (stages issued after it) * R loads are outstanding (the
   // attention-output loads issued in between only make this wait longer than needed).  The next
@@ -194,20 +196,20 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
   for (int s = 0; s < NS - 1; ++s) issue(s);
 
   // ---- x1 = x + o W_out^T; the attention output is read as B operands one stage ahead.  The
-  // accumulators start at zero and x (fp32, 4 DT 16-byte loads per lane) arrives in KO parts, part p
+  // accumulators start at zero and x (fp32, DT 16-byte loads per lane) arrives in KO parts, part p
   // requested after stage p-1's weights and added at the start of stage p+2 (the last two after
   // the loop): every block of a device pass starts at once, and waiting for the whole residual
   // before the first product would expose one chip-wide burst of reads per pass.
-  f32x16 acc[DT];
+  f32x4 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
-  constexpr int XP = 4 * DT / KO;   // 16-byte residual loads per part
-  static_assert(XP * KO == 4 * DT, "residual parts");
-  const float* xr = L.X + tload * D + 4 * h;
+    for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
+  constexpr int XP = DT / KO;   // 16-byte residual loads per part
+  static_assert(XP * KO == DT, "residual parts");
+  const float* xr = L.X + tload * D + 4 * qd;
   float4 xs[3][XP];
-  // residual 16-byte piece e = 4t + j holds accumulator tile t, elements 4j .. 4j+3
+  // residual piece t holds accumulator tile t (features 16t + 4(l/16) .. +3)
   // the wait counts below assume this issue order: keep the compiler from moving loads across
   auto order = [] {
     asm volatile("" ::: "memory");
@@ -217,34 +219,32 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     constexpr int p = decltype(p_)::value;
     order();
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int e = p * XP + i;
-      xs[p % 3][i] = *(const float4*)(xr + 32 * (e >> 2) + 8 * (e & 3));
-    }
+    for (int i = 0; i < XP; ++i) xs[p % 3][i] = *(const float4*)(xr + 16 * (p * XP + i));
   };
   auto add_x = [&](auto p_) {
     constexpr int p = decltype(p_)::value;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int e = p * XP + i, t = e >> 2, j = e & 3;
-      acc[t][4 * j + 0] += xs[p % 3][i].x;
-      acc[t][4 * j + 1] += xs[p % 3][i].y;
-      acc[t][4 * j + 2] += xs[p % 3][i].z;
-      acc[t][4 * j + 3] += xs[p % 3][i].w;
+      const int t = p * XP + i;
+      acc[t][0] += xs[p % 3][i].x;
+      acc[t][1] += xs[p % 3][i].y;
+      acc[t][2] += xs[p % 3][i].z;
+      acc[t][3] += xs[p % 3][i].w;
     }
   };
-  const T* orow = (const T*)L.O + tload * I + 8 * h;
-  frag ob[2][4];
+  // the attention output of the lane's token, K elements 8(l/16) .. +7 of each 32-wide K step
+  const T* orow = (const T*)L.O + tload * I + 8 * qd;
+  frag ob[2][2];
   order();
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) ob[0][ks] = *(const frag*)(orow + 16 * ks);
+  for (int ks = 0; ks < 2; ++ks) ob[0][ks] = *(const frag*)(orow + 32 * ks);
   load_x(std::integral_constant<int, 0>{});
   // loads issued after stage st's weights when stage st begins (in issue order: the weights of
   // stage 1, o of stage 0 and residual part 0 for st = 0; those plus stage 0's o, weights and part
   // for st = 1; then the part after the weights of st, and stage st-1's o, weights and part)
   auto wait_outproj = [&](auto st_) {
     constexpr int st = decltype(st_)::value;
-    constexpr int N = st == 0 ? R + 4 + XP : st == 1 ? R + 8 + 2 * XP : R + 4 + 2 * XP;
+    constexpr int N = st == 0 ? R + 2 + XP : st == 1 ? R + 4 + 2 * XP : R + 2 + 2 * XP;
     static_assert(N < 64, "vmcnt range");
     wait_vm<N>();
     block_barrier();
@@ -254,179 +254,161 @@ __global__ __launch_bounds__(256, 1) void block_kernel(BlockLaunch L) {
     wait_outproj(st_);
     if constexpr (st + 1 < KO)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ob[(st + 1) & 1][ks] = *(const frag*)(orow + 64 * (st + 1) + 16 * ks);
+      for (int ks = 0; ks < 2; ++ks) ob[(st + 1) & 1][ks] = *(const frag*)(orow + 64 * (st + 1) + 32 * ks);
     if constexpr (st >= 2) add_x(std::integral_constant<int, st - 2>{});
     const char* sl = smem + (st % NS) * SB + lane * 16;
     // fragment f = ks * DT + t
-    pipelined<4 * DT, GS, 0, frag>([&](int f) { return *(const frag*)(sl + f * 1024); },
-                                   [&](int f, const frag& a) { mma32(acc[f % DT], a, ob[st & 1][f / DT]); }, none);
+    pipelined<2 * DT, GS, 0, frag>([&](int f) { return *(const frag*)(sl + f * 1024); },
+                                   [&](int f, const frag& a) { mma(acc[f % DT], a, ob[st & 1][f / DT]); }, none);
     stage_end(st);
     if constexpr (st + 1 < KO) load_x(std::integral_constant<int, st + 1>{});
   });
   add_x(std::integral_constant<int, KO - 2>{});
   add_x(std::integral_constant<int, KO - 1>{});
 
-  // ---- RMSNorm_f(x1) as B operands (the gain is in W_1)
+  // ---- RMSNorm_f(x1) as B operands (the gain is in W_1): K step s takes, in lane group l/16,
+  // tiles 2s and 2s+1 (features 32s + 16(e/4) + 4(l/16) + e%4 for element e)
   float ss = 0.f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) ss = fmaf(acc[t][v], acc[t][v], ss);
+    for (int v = 0; v < 4; ++v) ss = fmaf(acc[t][v], acc[t][v], ss);
+  ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
   const float r1 = sqrtf((float)D) / fmaxf(sqrtf(ss), kNormEps);
-  frag xb[D / 16];
+  frag xb[D / 32];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
+  for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xb[s][e] = cvt<T>(acc[s >> 1][8 * (s & 1) + e] * r1);
+    for (int e = 0; e < 8; ++e) xb[s][e] = cvt<T>(acc[2 * s + e / 4][e & 3] * r1);
   if (q != 0) {   // only chunk group 0 carries x1; the others accumulate their chunks' part
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[t][v] = 0.f;
   }
 
   // ---- feed-forward onto x1, three chunks in flight: step c (stage KO + c, holding the W_1 rows
   // of chunk c and the W_2 columns of chunk c - 2) runs chunk c's first product, the GELU of chunk
-  // c-1's hidden tile and chunk c-2's second product, all independent of each other, so the GELU's
+  // c-1's hidden tiles and chunk c-2's second product, all independent of each other, so the GELU's
   // vector work fills the shadows of the products.  The loop is unrolled by two so the hidden-tile
-  // registers alternate without copies.  (A chain of dependent products on one accumulator runs
-  // at full rate on this matrix core, so the first product needs only one.)
-  constexpr int N1 = D / 16, N2 = 2 * DT;
-  f32x16 hA{}, hB{};
-  frag gA0{}, gA1{}, gB0{}, gB1{};
-  auto step = [&](auto do1_, auto dog_, auto do2_, const char* sl, int c, f32x16& n0, const f32x16& o0,
-                  frag& mk0, frag& mk1, const frag& us0, const frag& us1) {
+  // registers alternate without copies.
+  constexpr int N1 = D / 16, N2 = DT;
+  f32x4 hA[2] = {}, hB[2] = {};
+  frag gA{}, gB{};
+  auto step = [&](auto do1_, auto dog_, auto do2_, const char* sl, int c, f32x4 (&n0)[2], const f32x4 (&o0)[2],
+                  frag& mk, const frag& us) {
     constexpr bool do1 = decltype(do1_)::value, dog = decltype(dog_)::value, do2 = decltype(do2_)::value;
     constexpr int NA = do1 ? N1 : 0, NB = do2 ? N2 : 0, G = (NA + NB) / GS;
     if constexpr (do1) {
-      // the first product starts from b_1 (rows 8(v/4) + 4h + v%4 of chunk c), read before any
-      // fragment so that waiting for it never waits for those
-      const float* bb = b1s + 32 * c + 4 * h;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 b = *(const f32x4*)(bb + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) n0[4 * j + i] = b[i];
-      }
+      // the first product starts from b_1 (hidden features 32c + 16u + 4(l/16) + v of tile u), read
+      // before any fragment so that waiting for it never waits for those
+      const float* bb = b1s + 32 * c + 4 * qd;
+      n0[0] = *(const f32x4*)bb;
+      n0[1] = *(const f32x4*)(bb + 16);
     }
-    // second-product fragment k = f - NA: tile k % DT, K step k / DT (consecutive products go to
-    // different accumulators); the stream stores tile t's two K steps at 2t, 2t+1
-    auto rd = [&](int f) {
-      const int k = f - NA;
-      return *(const frag*)(sl + (f < NA ? f : N1 + 2 * (k % DT) + k / DT) * 1024);
-    };
+    // fragment f of the stage: W_1 tile f % 2, K step f / 2 (consecutive products go to different
+    // accumulators), then W_2 tile f - N1
+    auto rd = [&](int f) { return *(const frag*)(sl + (NA ? f : f + N1) * 1024); };
     auto mm = [&](int f, const frag& a) {
-      if (f < NA) {
-        mma32(n0, a, xb[f]);
-      } else {
-        const int k = f - NA;
-        mma32(acc[k % DT], a, (k / DT) ? us1 : us0);
-      }
+      if (f < NA) mma(n0[f & 1], a, xb[f >> 1]);
+      else mma(acc[f - NA], a, us);
     };
-    // GELU value v of the lane's 16 (hidden rows 8(v/4) + 4h + v%4 of chunk c-1) in region
-    // 1 + v G / 16 (all in "region 1" when there are no products)
+    // twice the GELU of value e of the lane's 8 (hidden features 16(e/4) + 4(l/16) + e%4 of chunk
+    // c-1) in region 1 + e G / 8 (all in "region 1" when there are no products)
     auto hook = [&](auto g_) {
       constexpr int g = decltype(g_)::value;
       if constexpr (dog) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (G == 0 || 1 + v * G / 16 == g) (v < 8 ? mk0 : mk1)[v & 7] = cvt<T>(gelu2_hidden(o0[v]));
+        for (int e = 0; e < 8; ++e)
+          if (G == 0 || 1 + e * G / 8 == g) mk[e] = cvt<T>(gelu2_hidden(o0[e >> 2][e & 3]));
       }
     };
     if constexpr (NA + NB == 0) {
       hook(std::integral_constant<int, 1>{});
     } else {
-      pipelined<NA + NB, GS, 8, frag>(rd, mm, hook);
+      pipelined<NA + NB, GS, C::VPM, frag>(rd, mm, hook);
     }
   };
   using Y = std::true_type;
   using Nn = std::false_type;
   // local step j (chunk c0 + j's first product, the GELU of the chunk before it, the second
   // product of the chunk two before it) with the register roles of its parity
-  auto run = [&](auto d1, auto dg, auto d2, int j, f32x16& n0, const f32x16& o0, frag& mk0, frag& mk1,
-                 const frag& us0, const frag& us1) {
+  auto run = [&](auto d1, auto dg, auto d2, int j, f32x4 (&n0)[2], const f32x4 (&o0)[2], frag& mk, const frag& us) {
     const char* sl = smem + ((KO + j) % NS) * SB + lane * 16;
-    step(d1, dg, d2, sl, c0 + j, n0, o0, mk0, mk1, us0, us1);
+    step(d1, dg, d2, sl, c0 + j, n0, o0, mk, us);
   };
   // j = 0, 1
   stage_begin(KO);
-  run(Y{}, Nn{}, Nn{}, 0, hA, hB, gA0, gA1, gB0, gB1);
+  run(Y{}, Nn{}, Nn{}, 0, hA, hB, gA, gB);
   stage_end(KO);
   stage_begin(KO + 1);
-  run(Y{}, Y{}, Nn{}, 1, hB, hA, gA0, gA1, gB0, gB1);
+  run(Y{}, Y{}, Nn{}, 1, hB, hA, gA, gB);
   stage_end(KO + 1);
   for (int j = 2; j < n; j += 2) {
     stage_begin(KO + j);
-    run(Y{}, Y{}, Y{}, j, hA, hB, gB0, gB1, gA0, gA1);
+    run(Y{}, Y{}, Y{}, j, hA, hB, gB, gA);
     stage_end(KO + j);
     stage_begin(KO + j + 1);
-    run(Y{}, Y{}, Y{}, j + 1, hB, hA, gA0, gA1, gB0, gB1);
+    run(Y{}, Y{}, Y{}, j + 1, hB, hA, gA, gB);
     stage_end(KO + j + 1);
   }
   stage_begin(KO + n);
-  run(Nn{}, Y{}, Y{}, n, hA, hB, gB0, gB1, gA0, gA1);
+  run(Nn{}, Y{}, Y{}, n, hA, hB, gB, gA);
   stage_end(KO + n);
   stage_begin(KO + n + 1);
-  run(Nn{}, Nn{}, Y{}, n + 1, hA, hB, gA0, gA1, gB0, gB1);
+  run(Nn{}, Nn{}, Y{}, n + 1, hA, hB, gA, gB);
 
   if (!ALL_CHUNKS && groups > 1) {   // this group's part of x2 - b_2, for the reduction kernel
     if (!valid) return;
-    float* pw = L.part + ((int64_t)q * (L.tokens - L.tok0) + (token - L.tok0)) * D + 4 * h;
+    float* pw = L.part + ((int64_t)q * (L.tokens - L.tok0) + (token - L.tok0)) * D + 4 * qd;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(float4*)(pw + 32 * t + 8 * j) = make_float4(acc[t][4 * j], acc[t][4 * j + 1], acc[t][4 * j + 2], acc[t][4 * j + 3]);
+    for (int t = 0; t < DT; ++t) *(float4*)(pw + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     return;
   }
 
   // ---- x2 = acc + b_2;  x3 = RMSNorm_out(x2) -> X;  XH = x3 normalised (or x3)
   {
-    const float* b2 = L.b2 + 4 * h;
+    const float* b2 = L.b2 + 4 * qd;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DT; ++t) {
+      const f32x4 b = *(const f32x4*)(b2 + 16 * t);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 b = *(const f32x4*)(b2 + 32 * t + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][4 * j + i] += b[i];
-      }
+      for (int i = 0; i < 4; ++i) acc[t][i] += b[i];
+    }
   }
   ss = 0.f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) ss = fmaf(acc[t][v], acc[t][v], ss);
+    for (int v = 0; v < 4; ++v) ss = fmaf(acc[t][v], acc[t][v], ss);
+  ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
   const float r2 = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-  const float* go = L.gout + 4 * h;
+  const float* go = L.gout + 4 * qd;
   float ss3 = 0.f;
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t) {
+    const f32x4 g = *(const f32x4*)(go + 16 * t);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 g = *(const f32x4*)(go + 32 * t + 8 * j);
+    for (int i = 0; i < 4; ++i) acc[t][i] *= r2 * g[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][4 * j + i] *= r2 * g[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss3 = fmaf(acc[t][4 * j + i], acc[t][4 * j + i], ss3);
-    }
+    for (int i = 0; i < 4; ++i) ss3 = fmaf(acc[t][i], acc[t][i], ss3);
+  }
+  ss3 += __shfl_xor(ss3, 16, 64);
   ss3 += __shfl_xor(ss3, 32, 64);
   const float r3 = L.xh_norm ? sqrtf((float)D) / fmaxf(sqrtf(ss3), kNormEps) : 1.0f;
   if (!valid) return;
-  float* xw = L.X + token * D + 4 * h;
-  T* hw = (T*)L.XH + token * D + 4 * h;
+  float* xw = L.X + token * D + 4 * qd;
+  T* hw = (T*)L.XH + token * D + 4 * qd;
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t) {
+    *(float4*)(xw + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    typename Vec4<T>::type h4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *(float4*)(xw + 32 * t + 8 * j) = make_float4(acc[t][4 * j], acc[t][4 * j + 1], acc[t][4 * j + 2], acc[t][4 * j + 3]);
-      typename Vec4<T>::type q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = cvt<T>(acc[t][4 * j + i] * r3);
-      *(typename Vec4<T>::type*)(hw + 32 * t + 8 * j) = q;
-    }
+    for (int i = 0; i < 4; ++i) h4[i] = cvt<T>(acc[t][i] * r3);
+    *(typename Vec4<T>::type*)(hw + 16 * t) = h4;
+  }
 }
 
 // x2 = b_2 + the chunk groups' parts (group 0 holds x1), then the epilogue of block_kernel:
@@ -503,7 +485,7 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
     L.tok0 = 0;
     L.groups = 1;
     const BlockLaunch Lm = [&] { BlockLaunch m = L; m.tokens = (int32_t)(L0.tokens - rest); return m; }();
-    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3((unsigned)(Lm.tokens / 128)), dim3(256), C::LDS, stream, Lm);
+    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3((unsigned)(Lm.tokens / 128)), dim3(C::THREADS), C::LDS, stream, Lm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rest == 0) return hipSuccess;
@@ -512,7 +494,7 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
   L.groups = tail_groups(tb, L0.ncu);
   if (L.groups > 1 && (!L.part || (size_t)L.groups * rest * C::D * 4 > block_part_bytes(C::D, L0.tokens, L0.ncu)))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((block_kernel<T, C, false>), dim3((unsigned)(tb * L.groups)), dim3(256), C::LDS, stream, L);
+  hipLaunchKernelGGL((block_kernel<T, C, false>), dim3((unsigned)(tb * L.groups)), dim3(C::THREADS), C::LDS, stream, L);
   if ((e = hipGetLastError()) != hipSuccess || L.groups == 1) return e;
   hipLaunchKernelGGL((block_reduce_kernel<T, C::D>), dim3((unsigned)((rest + 3) / 4)), dim3(256), 0, stream, L);
   return hipGetLastError();
@@ -521,7 +503,7 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
 template <typename T>
 hipError_t launch_dt(const BlockLaunch& L, hipStream_t stream) {
   // LDS reads in groups of 3 fragments (a sweep of 2, 3, 4, 6, 8, 12: 3 fastest, 8 about 3% slower)
-  if (L.D == 384 && L.I == 512) return launch_t<T, BlockCfg<T, 384, 512, 3, 3>>(L, stream);
+  if (L.D == 384 && L.I == 512) return launch_t<T, BlockCfg<T, 384, 512, 3, BLK_GS, BLK_VPM>>(L, stream);
   return hipErrorInvalidValue;
 }
 

@@ -311,44 +311,47 @@ int setup_tables_and_groups(mbr_core* c) {
 
 // Weights of the fused post-attention kernel (k_block.hip) as the stages it copies into LDS, each
 // stage D/8 fragments of 64 lanes x 8 elements in the order the lanes read them.  A fragment is
-// the A operand of one 32 x 32 x 16 product: lane l supplies row l % 32 and K elements
-// 8(l/32) .. 8(l/32)+7.
-//   stages 0 .. I/64-1: out-projection, K step ks of 4, tile t of D/32 (rows 32t..): W_out[row][k]
-//   stage I/64 + c:     W_1 rows of hidden chunk c (K steps s of D/16) with the columns permuted to
-//                       the accumulator's row order, then W_2 columns of chunk c-2 (tile t, step s2)
-//                       permuted to the order the hidden tile holds its rows, times 1/2 (the kernel's
-//                       hidden layer holds twice the GELU).
-// The accumulator of a 32 x 32 product holds in lane l rows 8(v/4) + 4(l/32) + v%4 (v = 0..15); read
-// as a B operand, K step s of a 32-row tile takes v = 8(s%2) + e, i.e. row
-// perm(s, h, e) = 32(s/2) + 8(2(s%2) + e/4) + 4h + e%4 for lane half h and element e.
+// the A operand of one 16 x 16 x 32 product: lane l supplies row l % 16 and K elements
+// 8(l/16) .. 8(l/16)+7.
+//   stages 0 .. I/64-1: out-projection, K step ks of 2, tile t of D/16 (rows 16t..): W_out[row][k]
+//   stage I/64 + c:     W_1 rows of hidden chunk c (fragment 2s + u: rows 32c + 16u.., K step s of
+//                       D/32) with the columns permuted to the accumulators' row order, then W_2
+//                       columns of chunk c-2 (fragment D/16 + t: rows 16t..) permuted to the order the
+//                       hidden tiles hold their rows, times 1/2 (the kernel's hidden layer holds
+//                       twice the GELU).
+// The accumulator of a 16 x 16 product holds in lane l rows 4(l/16) + v (v = 0..3); read as a B
+// operand, K step s of the residual takes tiles 2s and 2s+1, i.e. for lane group q = l/16 and
+// element e the row perm(s, q, e) = 32s + 16(e/4) + 4q + e%4, and the hidden chunk (two tiles) the
+// row 16(e/4) + 4q + e%4.
 std::vector<double> block_stream(int D, int I, int FF, const std::vector<double>& wout,
                                  const std::vector<double>& w1g, const std::vector<double>& w2) {
-  const int DT = D / 32, KO = I / 64, NCH = FF / 32;
+  const int DT = D / 16, KO = I / 64, NCH = FF / 32;
   const size_t stage = (size_t)D * 64;
   std::vector<double> out((size_t)(KO + NCH + 2) * stage, 0.0);
-  auto perm = [](int s, int h, int e) { return 32 * (s / 2) + 8 * (2 * (s % 2) + e / 4) + 4 * h + e % 4; };
+  auto perm = [](int s, int q, int e) { return 32 * s + 16 * (e / 4) + 4 * q + e % 4; };
   for (int st = 0; st < KO; ++st)
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
       for (int t = 0; t < DT; ++t)
         for (int l = 0; l < 64; ++l)
           for (int e = 0; e < 8; ++e) {
-            const int row = 32 * t + l % 32, k = 64 * st + 16 * ks + 8 * (l / 32) + e;
+            const int row = 16 * t + l % 16, k = 64 * st + 32 * ks + 8 * (l / 16) + e;
             out[st * stage + ((size_t)(ks * DT + t) * 64 + l) * 8 + e] = wout[(size_t)row * I + k];
           }
   for (int c = 0; c <= NCH + 1; ++c) {
     const size_t base = (size_t)(KO + c) * stage;
     if (c < NCH)
-      for (int s = 0; s < D / 16; ++s)
-        for (int l = 0; l < 64; ++l)
-          for (int e = 0; e < 8; ++e)
-            out[base + ((size_t)s * 64 + l) * 8 + e] = w1g[(size_t)(32 * c + l % 32) * D + perm(s, l / 32, e)];
-    if (c > 1)
-      for (int t = 0; t < DT; ++t)
-        for (int s2 = 0; s2 < 2; ++s2)
+      for (int s = 0; s < D / 32; ++s)
+        for (int u = 0; u < 2; ++u)
           for (int l = 0; l < 64; ++l)
             for (int e = 0; e < 8; ++e)
-              out[base + (size_t)(D / 16) * 512 + ((size_t)(2 * t + s2) * 64 + l) * 8 + e] =
-                  0.5 * w2[(size_t)(32 * t + l % 32) * FF + 32 * (c - 2) + perm(s2, l / 32, e)];
+              out[base + ((size_t)(2 * s + u) * 64 + l) * 8 + e] =
+                  w1g[(size_t)(32 * c + 16 * u + l % 16) * D + perm(s, l / 16, e)];
+    if (c > 1)
+      for (int t = 0; t < DT; ++t)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e)
+            out[base + ((size_t)(DT + t) * 64 + l) * 8 + e] =
+                0.5 * w2[(size_t)(16 * t + l % 16) * FF + 32 * (c - 2) + perm(0, l / 16, e)];
   }
   return out;
 }
