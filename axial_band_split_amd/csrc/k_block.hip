@@ -42,12 +42,6 @@ namespace mbr {
 
 namespace {
 
-#ifndef BLK_GS
-#define BLK_GS 3
-#endif
-#ifndef BLK_VPM
-#define BLK_VPM 4
-#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -502,15 +496,17 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_dt(const BlockLaunch& L, hipStream_t stream) {
-  // LDS reads in groups of 3 fragments (a sweep of 2, 3, 4, 6, 8, 12: 3 fastest, 8 about 3% slower)
-  if (L.D == 384 && L.I == 512) return launch_t<T, BlockCfg<T, 384, 512, 3, BLK_GS, BLK_VPM>>(L, stream);
+  // LDS reads in groups of 3 fragments, 4 vector instructions after each feed-forward product (group
+  // sizes 2, 3, 4 and 2, 4, 8 vector instructions time within 1%; 6 fragments about 1.5% slower)
+  if (L.D == 384 && L.I == 512) return launch_t<T, BlockCfg<T, 384, 512, 3, 3, 4>>(L, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// D = 512 fits the registers only with spills in the feed-forward loop; that width keeps the
-// separate products.
+// D = 512 needs more than the 256 registers of a wave that shares its SIMD (residual 128, normalised
+// operand 64, plus the hidden tiles and fragment buffers) and a 192 KB ring of three stages; that
+// width keeps the separate products.
 bool block_supported(int dtype, int D, int I, int FF) {
   return dtype != DT_F32 && FF == 4 * D && I == 512 && D == 384;
 }
