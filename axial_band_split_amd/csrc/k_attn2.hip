@@ -10,9 +10,9 @@
 //     into a 2-stage ring, the next tile in flight while the current one is consumed;
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16: a lane owns one query column and 16 of
 //     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart; the S^T
-//     accumulators start at minus the running reference, so a probability is one exponential, and
-//     the row sums come from the matrix core (a ones row times P^T), leaving the vector units the
-//     exponentials, the tile max and the conversions;
+//     accumulators start at minus the running reference, so a probability is one exponential; a
+//     lane adds up the fp32 probabilities it holds (one vector add each: the matrix core, already
+//     the busier unit, would spend a quarter more products on a ones-row sum at dh = 64);
 //   * the probabilities feed the P.V product straight from the S^T accumulators: the K rows of the
 //     S^T product are taken in a permuted order so that the 8 probabilities a lane holds for one
 //     16-key step belong to 8 consecutive keys, and the matching V^T operand is one 16-byte read;
@@ -149,17 +149,10 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
   for (int d = 0; d < DT; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[d][v] = 0.f;
-  // row sums of P on the matrix core: an A operand whose row 0 is all ones turns each P^T step
-  // into column sums, which land in row 0 of lsacc (lanes 0..31, element 0)
-  f32x16 lsacc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) lsacc[v] = 0.f;
-  frag ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = cvt<T>(l32 == 0 ? 1.0f : 0.0f);
   // q arrives scaled by log2(e) (and 1/sqrt(dh)), so scores are already in log2 units; the S^T
   // accumulators start at -mref, so the products deliver s - mref and p = exp2 of it directly
   float mref = 0.f;
+  float lsum_p = 0.f;   // the lane's part of its query's row sum (16 of every 32 keys)
   f32x16 negm;   // -mref in every element: the C operand of each tile's first S^T step
 #pragma unroll
   for (int v = 0; v < 16; ++v) negm[v] = 0.f;
@@ -206,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
         const float alpha = __builtin_amdgcn_exp2f(-up);
 #pragma unroll
         for (int d = 0; d < DT; ++d) o[d] *= alpha;
-        lsacc *= alpha;
+        lsum_p *= alpha;
       }
       mref += up;
 #pragma unroll
@@ -219,8 +212,11 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
       const int r = t >> 1, hv = (t & 1) * 8;
       frag pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(__builtin_amdgcn_exp2f(s[r][hv + e]));
-      mma32(lsacc, ones, pf);
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(s[r][hv + e]);
+        lsum_p += pe;
+        pf[e] = cvt<T>(pe);
+      }
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         // V^T row (head dim) d*32 + l32, keys 16t + 8g .. +7: one 16-byte chunk
@@ -231,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
     }
   }
 
-  const float lsum = __shfl(lsacc[0], l32, 64);
+  const float lsum = lsum_p + __shfl_xor(lsum_p, 32, 64);   // lanes l and l ^ 32 hold one query
   const int q = q0 + l32;
   if (q >= n) return;
   const size_t row = (size_t)seq * L.frames + q;
