@@ -129,6 +129,25 @@ struct GatherLaunch {
 };
 hipError_t launch_gather(const GatherLaunch& L, hipStream_t stream);
 
+// Band gather and band embedding in one kernel (k_embed.hip, 16-bit path): X = RMSNorm(gathered
+// band) W_i^T + b_i in fp32, XH = the same in 16 bits, ss = its row sums of squares per 64 columns.
+struct EmbedLaunch {
+  int dtype;
+  const float* in;            // the spectrum, io layout 0 or 1
+  const void* W;              // band weights in fragment order (see embed_stream in mbr_core.cpp)
+  const int32_t* w_off;       // [NB] element offset of band i's fragments from W
+  const int32_t* order;       // [NB] band indices, widest first
+  const int32_t* band_info;   // [NB][4] as for the gather
+  const int32_t* gather_pair; // slot -> pair
+  const float* bias;          // [NB][D]
+  float* X;                   // [NB][batch * frames][D]
+  void* XH;                   // same, 16-bit
+  float* ss;                  // [NB * batch * frames][kSsStride]
+  int32_t num_bands, batch, frames, n_freqs, channels, layout, D, max_kpad;
+};
+bool embed_fused_supported(int dtype, int D, int max_kpad);
+hipError_t launch_embed(const EmbedLaunch& L, hipStream_t stream);
+
 // Attention over sequences held in [seqs][H][npad][dh] (q, k, v);
 // writes O * gate into token layout O[row][H*dh].
 struct AttnLaunch {

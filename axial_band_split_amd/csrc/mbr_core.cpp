@@ -125,12 +125,15 @@ struct mbr_core {
   int glu_blk = 16;                   // value / gate pairing block of the last mask layer
   bool use_block = false;             // 16-bit path with the fused post-attention kernel
   bool use_band = false;              // 16-bit path: band axis' projection and attention in one kernel
+  bool use_embed = false;             // 16-bit path: band gather and embedding in one kernel
   int kpad_total = 0, kpad_max = 0;
   // device memory
   char* wdev = nullptr;               // dtype weights
   float* fdev = nullptr;              // fp32 side tables
   size_t emb_w = 0, emb_b = 0;
   std::vector<size_t> emb_wband;
+  size_t emb_frag = 0;                // fused embedding: fragment-ordered band weights, all bands
+  std::vector<int32_t> emb_foff;      // per band: element offset of its fragments from emb_frag
   std::vector<TransformerW> tw;
   std::vector<MaskW> mw;              // per stem
   void* ws = nullptr;                 // workspace block
@@ -152,6 +155,8 @@ struct mbr_core {
   // tables
   int32_t* band_info = nullptr;
   int32_t* gather_pair = nullptr;
+  int32_t* emb_woff = nullptr;        // [NB] (fused embedding)
+  int32_t* band_order = nullptr;      // [NB] bands, widest first (fused embedding)
   int32_t* inv_slot = nullptr;
   float* inv_weight = nullptr;
   float *cos_t = nullptr, *sin_t = nullptr, *cos_b = nullptr, *sin_b = nullptr;
@@ -203,7 +208,7 @@ int setup_tables_and_groups(mbr_core* c) {
   };
   c->g_embed = 0;
   c->t_embed = 0;
-  for (int i = 0; i < c->NB; ++i) {
+  for (int i = 0; i < (c->use_embed ? 0 : c->NB); ++i) {
     GemmGroup g{};
     g.a_off0 = 0;
     g.a_offb = c->kcol[i];
@@ -278,11 +283,20 @@ int setup_tables_and_groups(mbr_core* c) {
     off = o + bytes;
     return o;
   };
+  // fused embedding: band weight offsets and the bands widest first
+  std::vector<int32_t> order(c->NB);
+  for (int i = 0; i < c->NB; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return c->kpad[a] > c->kpad[b]; });
+  std::vector<int32_t> woff = c->emb_foff;
+  woff.resize(c->NB, 0);
+  size_t o_woff = place(woff.size() * 4), o_ord = place(order.size() * 4);
   size_t o_info = place(info.size() * 4), o_gp = place(bd.gather_pair.size() * 4),
          o_inv = place(bd.inv_slot.size() * 4), o_w = place(bd.inv_weight.size() * 4), o_ct = place(ct.size() * 4),
          o_st = place(st.size() * 4), o_cb = place(cb.size() * 4), o_sb = place(sb.size() * 4),
          o_g = place(groups.size() * sizeof(GemmGroup)), o_t = place(tiles.size() * sizeof(GemmTile));
   std::vector<char> host(off);
+  std::memcpy(host.data() + o_woff, woff.data(), woff.size() * 4);
+  std::memcpy(host.data() + o_ord, order.data(), order.size() * 4);
   std::memcpy(host.data() + o_info, info.data(), info.size() * 4);
   std::memcpy(host.data() + o_gp, bd.gather_pair.data(), bd.gather_pair.size() * 4);
   std::memcpy(host.data() + o_inv, bd.inv_slot.data(), bd.inv_slot.size() * 4);
@@ -296,6 +310,8 @@ int setup_tables_and_groups(mbr_core* c) {
   HIP_TRY(hipMalloc(&c->tables_dev, off));
   HIP_TRY(hipMemcpy(c->tables_dev, host.data(), off, hipMemcpyHostToDevice));
   char* b = c->tables_dev;
+  c->emb_woff = (int32_t*)(b + o_woff);
+  c->band_order = (int32_t*)(b + o_ord);
   c->band_info = (int32_t*)(b + o_info);
   c->gather_pair = (int32_t*)(b + o_gp);
   c->inv_slot = (int32_t*)(b + o_inv);
@@ -356,6 +372,22 @@ std::vector<double> block_stream(int D, int I, int FF, const std::vector<double>
   return out;
 }
 
+// One band's embedding weights (m: D rows x kp columns) in the order the fused embedding kernel
+// (k_embed.hip) reads them: wave w of 4 (features D/4 w ..), K step ks of 16, tile ft of 32
+// features, then 64 lanes x 8 elements of the A operand of a 32 x 32 x 16 product (lane l: feature
+// D/4 w + 32 ft + l % 32, K elements 16 ks + 8(l/32) ..).
+std::vector<double> embed_stream(int D, int kp, const std::vector<double>& m) {
+  std::vector<double> out((size_t)D * kp);
+  const int fpw = D / 4, ft_n = fpw / 32;
+  size_t o = 0;
+  for (int w = 0; w < 4; ++w)
+    for (int ks = 0; ks < kp / 16; ++ks)
+      for (int ft = 0; ft < ft_n; ++ft)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) out[o++] = m[(size_t)(fpw * w + 32 * ft + l % 32) * kp + 16 * ks + 8 * (l / 32) + e];
+  return out;
+}
+
 int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
   const mbr_config& cfg = c->cfg;
   const Bands& bd = c->bands;
@@ -365,7 +397,8 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
   size_t idx = 0;
   // band embedding: fold gamma_i * sqrt(W_i) into the projection, pad K to kpad_i
   c->emb_wband.resize(c->NB);
-  std::vector<double> emb_bias;
+  c->emb_foff.resize(c->NB);
+  std::vector<double> emb_bias, emb_frag;
   for (int i = 0; i < c->NB; ++i) {
     const std::vector<double>& g = W[idx++];
     const std::vector<double>& A = W[idx++];
@@ -375,10 +408,17 @@ int repack_weights(mbr_core* c, const std::vector<std::vector<double>>& W) {
     std::vector<double> m((size_t)D * kp, 0.0);
     for (int d = 0; d < D; ++d)
       for (int e = 0; e < Wi; ++e) m[(size_t)d * kp + e] = A[(size_t)d * Wi + e] * g[e] * r;
-    c->emb_wband[i] = pk.append(m);
+    if (c->use_embed) {
+      c->emb_foff[i] = (int32_t)emb_frag.size();
+      const std::vector<double> f = embed_stream(D, kp, m);
+      emb_frag.insert(emb_frag.end(), f.begin(), f.end());
+    } else {
+      c->emb_wband[i] = pk.append(m);
+    }
     emb_bias.insert(emb_bias.end(), b.begin(), b.end());
   }
   c->emb_b = fp.append(emb_bias);
+  if (c->use_embed) c->emb_frag = pk.append(emb_frag);
   // transformers: attention gain (and the query scale dh^-1/2) folded into W_qkv and the gate
   // weights; feed-forward gain into W_1; output gain times sqrt(D) kept as a vector
   const double qscale = 1.0 / std::sqrt((double)c->DH);
@@ -480,7 +520,7 @@ int alloc_workspace(mbr_core* c) {
   const size_t attn_t = (size_t)c->NB * c->Bmax * c->H * c->Tp * c->DH * esz;
   const size_t attn_b = c->use_band ? 0 : BT * c->H * 64 * c->DH * esz;   // unused by the fused band kernel
   size_t oX = place(NT * c->D * 4), oXH = place(NT * c->D * esz), oG = place(NT * c->H * 4),
-         oU = place(BT * c->kpad_total * esz), oqt = place(attn_t), okt = place(attn_t), ovt = place(attn_t),
+         oU = place(c->use_embed ? 0 : BT * c->kpad_total * esz), oqt = place(attn_t), okt = place(attn_t), ovt = place(attn_t),
          oqb = place(attn_b), okb = place(attn_b), ovb = place(attn_b), oO = place(NT * c->I * esz),
          oH1 = place(NT * std::max(c->FF, c->cfg.num_stems * c->MH) * esz),
          oH2 = place(NT * c->cfg.num_stems * c->MH * esz),
@@ -558,28 +598,53 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
   const int parts = c->D / 64;
   const float sqrtD = std::sqrt((float)c->D);
 
-  GatherLaunch gl{dt, in, c->U, c->band_info, c->gather_pair, c->NB, batch, c->T, c->bands.n_freqs,
-                  c->bands.channels, cfg.io_layout, c->kpad_max};
-  LAUNCH(MBR_K_GATHER, launch_gather(gl, s));
+  if (c->use_embed) {
+    // the band gather and the band embedding in one kernel: the gathered bands stay on the chip
+    EmbedLaunch el{};
+    el.dtype = dt;
+    el.in = in;
+    el.W = wptr(c->emb_frag);
+    el.w_off = c->emb_woff;
+    el.order = c->band_order;
+    el.band_info = c->band_info;
+    el.gather_pair = c->gather_pair;
+    el.bias = c->fdev + c->emb_b;
+    el.X = c->X;
+    el.XH = c->XH;
+    el.ss = c->ssB;     // x0's row sums of squares: the first attention's input norm
+    el.num_bands = c->NB;
+    el.batch = batch;
+    el.frames = c->T;
+    el.n_freqs = c->bands.n_freqs;
+    el.channels = c->bands.channels;
+    el.layout = cfg.io_layout;
+    el.D = c->D;
+    el.max_kpad = c->kpad_max;
+    LAUNCH(MBR_K_EMBED, launch_embed(el, s));
+  } else {
+    GatherLaunch gl{dt, in, c->U, c->band_info, c->gather_pair, c->NB, batch, c->T, c->bands.n_freqs,
+                    c->bands.channels, cfg.io_layout, c->kpad_max};
+    LAUNCH(MBR_K_GATHER, launch_gather(gl, s));
 
-  GemmLaunch ge{};
-  ge.dtype = dt;
-  ge.epi = EPI_EMBED;
-  ge.A = c->U;
-  ge.B = W;
-  ge.C = c->X;
-  ge.bias = c->fdev;
-  ge.ldc = c->D;
-  ge.M = BT;
-  ge.groups = c->groups;
-  ge.tiles = c->tiles + c->t_embed;
-  ge.n_tiles = c->n_embed;
-  if (fused) {
-    ge.xh = c->XH;     // x0 in 16 bits and its row sums of squares: the first attention's input
-    ge.ss1 = c->ssB;
-    ge.ss_parts = parts;
+    GemmLaunch ge{};
+    ge.dtype = dt;
+    ge.epi = EPI_EMBED;
+    ge.A = c->U;
+    ge.B = W;
+    ge.C = c->X;
+    ge.bias = c->fdev;
+    ge.ldc = c->D;
+    ge.M = BT;
+    ge.groups = c->groups;
+    ge.tiles = c->tiles + c->t_embed;
+    ge.n_tiles = c->n_embed;
+    if (fused) {
+      ge.xh = c->XH;     // x0 in 16 bits and its row sums of squares: the first attention's input
+      ge.ss1 = c->ssB;
+      ge.ss_parts = parts;
+    }
+    LAUNCH(MBR_K_EMBED, gemm(ge, c->v_embed, s));
   }
-  LAUNCH(MBR_K_EMBED, gemm(ge, c->v_embed, s));
 
   if (!fused) {
     NormLaunch nl{dt, 0, c->X, c->XH, nullptr, c->gates, c->fdev + c->tw[0].wg, c->fdev + c->tw[0].bg, NT, c->D, c->H};
@@ -950,6 +1015,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
     c->wp[i] = round_up(c->bands.width[i], c->glu_blk);
   }
   c->kpad_total = col;
+  c->use_embed = embed_fused_supported(cfg->dtype, c->D, c->kpad_max);
   // read the caller's weights
   std::vector<std::vector<double>> W(inv.size());
   const size_t esz = dtype_size(cfg->dtype);

@@ -194,7 +194,7 @@ def roofline_md(stats_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, s
             busy = mb / (N_SIMD * ga / N_XCD)
         except SystemExit:
             pass
-        if kind in R.MFMA_KINDS:
+        if kind in R.MFMA_KINDS and not (kind == "embed" and "embed_kernel" in " ".join(names)):
             f = flops[kind]
             ach = f / (avg_us * 1e-6) / 1e12
             work, achs, frac = f"{f / 1e9:.1f} GFLOP", f"{ach:.0f} TFLOP/s", ach / R.PEAK_MFMA_TFLOPS[w.dtype]

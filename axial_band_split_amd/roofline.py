@@ -55,7 +55,7 @@ def shape_of(w: synth.Workload, total_width: int, batch: int | None = None) -> S
 
 # rocprofv3 kernel-name patterns of each kernel class on the 16-bit path (the GEMM's epilogue id is
 # its second template argument)
-KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E", "qkv": r"gemm2_kernelIDF16b?_?Li1E",
+KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E|embed_kernel", "qkv": r"gemm2_kernelIDF16b?_?Li1E",
               "ffn1": r"gemm2_kernelIDF16b?_?Li2E", "out_proj": r"gemm2_kernelIDF16b?_?Li3E",
               "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
               "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
@@ -108,6 +108,9 @@ def bytes_per_launch(s: Shape) -> Dict[str, float]:
     spec = 4.0 * BT * s.n_freqs * s.channels * 2
     return {
         "gather": spec + BT * s.total_width * s.esz,
+        # band gather and embedding in one kernel (16-bit path): the spectrum read once, x0 written in
+        # fp32 and in 16 bits
+        "embed": spec + N * D * 4.0 + N * D * s.esz,
         "norm_pre": N * D * 4.0 + N * D * s.esz,                 # read x, write x^
         "norm_out": N * D * 4.0 * 2 + N * D * s.esz,             # read x, write x and x^
         "average": 4.0 * s.stems * BT * s.total_width + s.stems * spec,

@@ -168,6 +168,31 @@ def test_half_precision_block_path_stage_taps(dtype):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,layout", [(synth.F16, synth.IO_FS_T_C), (synth.F16, synth.IO_SC_F_T),
+                                          (synth.BF16, synth.IO_SC_F_T)])
+def test_fused_band_embedding_against_oracle(dtype, layout):
+    """The band gather and embedding kernel of the 16-bit path: x0 of every band against the oracle's
+    band split, at 97 frames and two chunks (row blocks of 64 that straddle the chunks and end
+    ragged), in both input layouts, with band norms over unequal inputs (std 0.05 weights, gains
+    0.3 apart)."""
+    w = synth.WORKLOADS["t256_fp16"].replace(frames=97, batch=2, depth=1, dtype=dtype, io_layout=layout)
+    say(f"[embed] {synth.DTYPE_NAMES[dtype]} layout {layout}, B=2, T=97")
+    cfg, ws = build(w, std=0.05, gamma_std=0.3)
+    x = synth.draw_input(w)
+    taps = M.Taps()
+    M.forward(x, ocfg(w), ws, taps=taps)
+    core = binding.Core(cfg, ws)
+    xd = torch.from_numpy(synth.input_in_layout(w, x)).cuda()
+    B, T, NB, D = taps.embed.shape
+    got = core.debug(xd, 0).cpu().numpy().reshape(NB, B, T, D)
+    core.close()
+    ref = taps.embed.transpose(2, 0, 1, 3)
+    e = rel_l2(got, ref)
+    worst = max(rel_l2(got[i], ref[i]) for i in range(NB))
+    say(f"[embed] rel L2 = {e:.2e}, worst band {worst:.2e}")
+    assert e < (2e-3 if dtype == synth.F16 else 1e-2) and worst < (4e-3 if dtype == synth.F16 else 2e-2)
+
+
 def test_batch_below_max_and_sc_f_t_layout():
     w = synth.WORKLOADS["tiny_fp32"].replace(batch=3, io_layout=synth.IO_SC_F_T)
     say("[parity] tiny layout 1, max_batch 3, batches 3, 2, 1")
