@@ -370,6 +370,38 @@ __global__ __launch_bounds__(256) void average_kernel(AverageLaunch L) {
   }
 }
 
+// The same with four consecutive frames per thread (16-byte reads of the masks, 32 contiguous bytes
+// written per thread in the (pair, frame, re / im) layout) and one wave per workgroup, when the
+// frame count is a multiple of 4: a quarter of the threads and memory instructions.
+__global__ __launch_bounds__(64) void average4_kernel(AverageLaunch L) {
+  const int t = (blockIdx.x * 64 + threadIdx.x) * 4;
+  const int p = blockIdx.y;                   // pair f*S + s
+  const int bs = blockIdx.z;                  // b * stems + stem
+  if (t >= L.frames) return;
+  const int T_ = L.frames, S = L.channels, F = L.n_freqs;
+  const int b = bs / L.stems, st = bs - b * L.stems;
+  const int s1 = L.inv_slot[2 * p], s2 = L.inv_slot[2 * p + 1];
+  const float w = L.inv_weight[p];
+  const float* M = L.M + ((size_t)st * L.batch + b) * (size_t)L.total * T_;
+  f32x4 re = *(const f32x4*)(M + (size_t)(2 * s1) * T_ + t), im = *(const f32x4*)(M + (size_t)(2 * s1 + 1) * T_ + t);
+  if (s2 >= 0) {
+    re += *(const f32x4*)(M + (size_t)(2 * s2) * T_ + t);
+    im += *(const f32x4*)(M + (size_t)(2 * s2 + 1) * T_ + t);
+  }
+  re *= w;
+  im *= w;
+  if (L.layout == 0) {
+    f32x4* o = (f32x4*)(L.out + (((size_t)bs * F * S + p) * T_ + t) * 2);
+    o[0] = f32x4{re[0], im[0], re[1], im[1]};
+    o[1] = f32x4{re[2], im[2], re[3], im[3]};
+  } else {
+    const int f = p / S, s = p - f * S;
+    float* base = L.out + ((size_t)bs * S * 2 + s * 2) * (size_t)F * T_ + (size_t)f * T_ + t;
+    *(f32x4*)base = re;
+    *(f32x4*)(base + (size_t)F * T_) = im;
+  }
+}
+
 __global__ __launch_bounds__(256) void gelu_kernel(const float* x, float* y, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) y[i] = gelu_erf(x[i]);
@@ -432,6 +464,11 @@ hipError_t launch_gather(const GatherLaunch& L, hipStream_t stream) {
 }
 
 hipError_t launch_average(const AverageLaunch& L, hipStream_t stream) {
+  if (L.frames % 4 == 0) {   // rows of the masks and of the output then start 16-byte aligned
+    dim3 grid((L.frames / 4 + 63) / 64, L.n_freqs * L.channels, L.batch * L.stems), block(64);
+    hipLaunchKernelGGL(average4_kernel, grid, block, 0, stream, L);
+    return hipGetLastError();
+  }
   dim3 grid((L.frames + 255) / 256, L.n_freqs * L.channels, L.batch * L.stems), block(256);
   hipLaunchKernelGGL(average_kernel, grid, block, 0, stream, L);
   return hipGetLastError();
