@@ -1,4 +1,5 @@
-"""Coefficients of the hidden-layer GELU of the fused post-attention kernel (k_block.hip).
+"""Coefficients of the 16-bit GELU (gelu2_tail in kcommon.h: the fused post-attention kernel and the
+GEMM's GELU epilogue).
 
 GELU(x) = x Phi(x) = max(x, 0) - |x| Q(|x|), Q the upper tail of the standard normal distribution.
 The kernel takes Q(a) = 2^(p(a) - 1), p(a) = c3 a^3 + c2 a^2 + c1 a (so Q(0) = 1/2 exactly), and this

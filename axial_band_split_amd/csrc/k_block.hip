@@ -8,7 +8,8 @@
 //
 // ([P1] "Per Attention layer", "The forward chain"; [P5] export-roformer.py classes Attn, FF and
 // Block: the residual adds, the erf GELU feed-forward and the RMSNorm with its 1e-12 clamp.  The
-// GELU is evaluated to 1.3e-4 here, below the 16-bit rounding of the hidden layer; see gelu2_hidden.)
+// hidden layer holds twice the GELU, evaluated to 1.3e-4 by gelu2_tail (below the 16-bit rounding
+// of the hidden layer), and the W_2 columns of the weight stream carry the factor 1/2, which is exact.)
 //
 // Tokens are the N side of every product: a wave owns 16 tokens and keeps, for all of them,
 // the whole residual row in its accumulators (D/16 tiles of 16 x 16 on v_mfma_f32_16x16x32; lane
@@ -97,24 +98,6 @@ __device__ __forceinline__ void pipelined(RD rd, MM mm, HK hook) {
     }
     __builtin_amdgcn_sched_barrier(0);
   }, std::make_integer_sequence<int, G>{});
-}
-
-// Twice the GELU of the hidden layer (the W_2 columns of the weight stream carry the factor 1/2,
-// which is exact): 2 x Phi(x) = x + |x| (1 - 2 Q(|x|)), Q the upper tail of the standard normal
-// distribution, with 2 Q(a) = 2^p(a) for a cubic p without constant term (so 2 Q(0) = 1 exactly); its
-// three coefficients are a minimax fit of the weighted error max(a, 1) |2^(p(a) - 1) - Q(a)| over
-// [0, 10] (gelu_tail_fit.py beside this file).  All three are negative, so p falls for every a >= 0
-// and the tail goes to zero.  The GELU is within 1.3e-4 absolute and 1.3e-4 |x| of the erf GELU
-// everywhere, below the 16-bit rounding of the hidden layer (a relative step of 4.9e-4 in fp16); for
-// large negative x the sum cancels to within 1e-7 absolute.  Four vector instructions, one exp2 and
-// the add that also rounds to 16 bits per value: the vector work per product is what bounds this
-// kernel's issue rate.
-__device__ __forceinline__ float gelu2_hidden(float x) {
-  const float a = fabsf(x);
-  float p = fmaf(-0.030005693f, a, -0.48125008f);
-  p = fmaf(p, a, -1.1454322f);
-  p *= a;
-  return fmaf(a, 1.0f - __builtin_amdgcn_exp2f(p), x);
 }
 
 template <typename T, int D_, int I_, int NS_, int GS_, int VPM_>
@@ -315,7 +298,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void block_kernel(BlockLaunch L) {
       if constexpr (dog) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (G == 0 || 1 + e * G / 8 == g) mk[e] = cvt<T>(gelu2_hidden(o0[e >> 2][e & 3]));
+          if (G == 0 || 1 + e * G / 8 == g) mk[e] = cvt<T>(gelu2_tail(o0[e >> 2][e & 3]));
       }
     };
     if constexpr (NA + NB == 0) {

@@ -443,7 +443,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm2_kernel(GemmLaunch L) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float xv = v[e] + bvals[e];
-            if constexpr (EPI == EPI_GELU) p[e] = cvt<T>(gelu_erf(xv));
+            if constexpr (EPI == EPI_GELU) p[e] = cvt<T>(0.5f * gelu2_tail(xv));   // rounded to 16 bits
             else if constexpr (EPI == EPI_TANH) p[e] = cvt<T>(tanh_fast(xv));
             else p[e] = cvt<T>(xv);
           }
