@@ -11,8 +11,9 @@
 // Workgroup = (FR frames, head h), two waves per frame (FR = 2).  The FR x 64 band slots of the
 // frames (bands >= NB are padding rows, read as a valid row and masked as keys) are the rows of a
 // 64 FR x 192 x D product
-// against the head's rows of W_qkv ([q_h | k_h | v_h]); K goes through a 3-stage LDS ring by 16-byte
-// direct loads, as in the GEMM.  Wave (f, r) owns the 32 band slots 32r .. 32r+31 of frame f and all
+// against the head's rows of W_qkv ([q_h | k_h | v_h]); K goes through a 2-stage LDS ring by 16-byte
+// direct loads, as in the GEMM (the next step's loads in flight during each step; three workgroups
+// per compute unit hide the rest of the latency).  Wave (f, r) owns the 32 band slots 32r .. 32r+31 of frame f and all
 // 192 columns (six 32 x 32 tiles on v_mfma_f32_32x32x16):
 //   * the q and k tiles are taken transposed (features x tokens), so a lane holds one token and four
 //     consecutive features per group: the rotary pairs are in the lane, and the accumulator read in
@@ -21,8 +22,9 @@
 //   * the v tiles are taken as tokens x features, which read the same way are the V^T operand of
 //     O^T = V^T P^T whose key order matches the probabilities straight from the S^T accumulators;
 //   * the two waves of a frame swap their keys' k and v fragments through LDS (8 KB each);
-//   * the gate of each token is a dot product on the vector units, read from the same LDS tiles of
-//     x^ during the K loop (two lanes per token, half the K step each).
+//   * the gate of each token is a dot product on the vector units over the A fragments the product
+//     already holds (two lanes per token, half the K step each; packed 16-bit dot instructions with
+//     fp32 accumulation).
 // The softmax runs over one tile of 64 keys (the 60 bands of a frame) in registers; the output goes
 // out through a per-wave LDS staging as 16-byte rows.
 #include "kcommon.h"
@@ -49,6 +51,22 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// sum_e a[e] b[e] + c over eight 16-bit pairs: the products are exact in fp32
+__device__ __forceinline__ float dot8(const f16x8& a, const f16x8& b, float c) {
+  typedef f16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_fdot2(h2{a[2 * i], a[2 * i + 1]}, h2{b[2 * i], b[2 * i + 1]}, c, false);
+  return c;
+}
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float c) {
+  typedef bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_fdot2_f32_bf16(b2{a[2 * i], a[2 * i + 1]}, b2{b[2 * i], b[2 * i + 1]}, c, false);
+  return c;
+}
+
 // 16-byte chunks of a 64-byte LDS row, XOR-permuted so the 32 rows of a fragment read spread over
 // the banks (the GEMM's layout)
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -62,10 +80,15 @@ struct BandCfg {
   static constexpr int kCols = 192;                      // [q_h | k_h | v_h], dh = 64
   static constexpr int kWaves = 2 * FR, kThreads = 64 * kWaves;
   static constexpr int kStage = (kRows + kCols) * 64;    // one K step of 32
-  static constexpr int kNS = 3;
+  static constexpr int kNS = 2;
+  static constexpr int kOcc = 3;                         // workgroups per compute unit (LDS, VGPRs)
   static constexpr int kExch = kWaves * 8192;            // per wave: its keys' 4 k and 4 v fragments
   static constexpr int kOut = kWaves * 4096;             // per wave: 32 tokens x 64 outputs, 16-bit
   static constexpr int kLds = (kNS * kStage > kExch + kOut ? kNS * kStage : kExch + kOut);
+  // past the ring, free until the output staging: the gate weights (D <= 1024, 16-bit) and the
+  // rotary rows of positions 0..7 and 0, 8, .., 56
+  static constexpr int kAux = kNS * kStage;
+  static_assert(kAux + 8192 <= kLds, "auxiliary tables fit past the ring");
   static constexpr int kALoads = kRows * 4 / kThreads;   // 16-byte A loads per thread per stage (2)
   static constexpr int kBChunks = kCols * 4;             // 768
   static constexpr int kBLoads = (kBChunks + kThreads - 1) / kThreads;
@@ -73,13 +96,12 @@ struct BandCfg {
 };
 
 template <typename T, int FR>
-__global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch L) {
+__global__ __launch_bounds__(128 * FR, BandCfg<FR>::kOcc) void band_attn_kernel(BandLaunch L) {
   using C = BandCfg<FR>;
   constexpr int kRows = C::kRows, kCols = C::kCols, kStage = C::kStage, kNS = C::kNS, kExch = C::kExch,
                 NT = C::kThreads, NW = C::kWaves;
   using frag = typename Frag<T>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ __attribute__((aligned(16))) float wg[1024];   // the head's gate weights (D <= 1024)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -93,7 +115,15 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
   const int logical = xcd * per + min(xcd, rem) + slot;
   const int h = logical % L.heads, f0 = (logical / L.heads) * FR;
 
-  for (int i = tid; i < D; i += NT) wg[i] = tof<T>(((const T*)L.W)[(size_t)(3 * I + h) * D + i]);
+  T* wg = (T*)(smem + C::kAux);                             // the head's gate weights
+  float4* rt = (float4*)(smem + C::kAux + 4096);            // [16][16]: (cos, sin) of pairs 2q, 2q+1
+  for (int i = tid; i < D; i += NT) wg[i] = ((const T*)L.W)[(size_t)(3 * I + h) * D + i];
+  for (int i = tid; i < 256; i += NT) {     // row r: position r (r < 8) or 8 (r - 8)
+    const int r = i >> 4, q = i & 15, pos = r < 8 ? r : 8 * (r - 8);
+    const float2 c = *(const float2*)(L.cos + pos * 32 + 2 * q);
+    const float2 sn = *(const float2*)(L.sin + pos * 32 + 2 * q);
+    rt[i] = make_float4(c.x, sn.x, c.y, sn.y);
+  }
   __syncthreads();
 
   // ---- loader.  A row rho: frame f0 + rho/64, band slot rho%64 -> token slot*BT + frame (padding
@@ -126,7 +156,7 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
       if (j < C::kBLoads - 1 || blast) buffer_dma16(brs, voff[C::kALoads + j], ko, base + kRows * 64 + (j * NW + wu) * 1024);
   };
 
-  // ---- the 256 x 192 product; this wave: rows 64 fl + 32 half + (0..31), all six column tiles.
+  // ---- the 64 FR x 192 product; this wave: rows 64 fl + 32 half + (0..31), all six column tiles.
   // Tiles 0..3 (q, k) as C^T = W X^T, tiles 4, 5 (v) as C = X W^T.
   f32x16 acc[6];
 #pragma unroll
@@ -136,17 +166,30 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
   float gdot = 0.f;                         // gate: this lane's token, K half hl of every step
   const int arow = 64 * fl + 32 * half + r32;
   const int nk = D >> 5;
+  // row scale of this lane's token (x^ not yet normalised: sqrt(D) / |x|), its statistics read with
+  // the first stage
+  const int slot_me = 32 * half + r32;                  // this lane's band slot (token of tiles 0..3)
+  const int fr = f0 + fl;
+  const int64_t token = (int64_t)min(slot_me, NB - 1) * BT + min(fr, BT - 1);
+  float4 rs[4];
+  if (L.rowss) {
+    const float4* p = (const float4*)(L.rowss + token * kSsStride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = p[i];
+  }
   issue(0);
-  if (nk > 1) issue(1);
+  wait_vm<0>();
+  float sc = 1.0f;
+  if (L.rowss) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += (rs[i].x + rs[i].y) + (rs[i].z + rs[i].w);
+    sc = L.rs_mul / fmaxf(sqrtf(ss), kNormEps);
+  }
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) {                      // at most the next stage's loads outstanding
-      if (blast) wait_vm<C::kALoads + C::kBLoads>();
-      else wait_vm<C::kALoads + C::kBLoads - 1>();
-    } else {
-      wait_vm<0>();
-    }
-    block_barrier();
-    if (ks + 2 < nk) issue(ks + 2);         // the slot of step ks-1, read by every wave before the barrier
+    if (ks) wait_vm<0>();                   // this wave's loads of step ks
+    block_barrier();                        // everyone's; and every wave is done with step ks-1
+    if (ks + 1 < nk) issue(ks + 1);         // into the slot of step ks-1
     const char* st = smem + (ks % kNS) * kStage;
     frag a[2], b[2][6];
 #pragma unroll
@@ -159,16 +202,9 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
         b[kh][j] = *(const frag*)(st + kRows * 64 + brow * 64 + ((lc ^ swz(brow)) << 4));
       }
     }
-    // gate: elements 16 hl .. 16 hl + 15 of this step for the lane's token (chunks 2 hl, 2 hl + 1)
-    {
-      const frag g0 = *(const frag*)(st + arow * 64 + (((2 * hl) ^ swz(arow)) << 4));
-      const frag g1 = *(const frag*)(st + arow * 64 + (((2 * hl + 1) ^ swz(arow)) << 4));
-      const float* wk = wg + ks * 32 + 16 * hl;
+    // gate: chunks hl and 2 + hl of this step for the lane's token, the A fragments
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gdot = fmaf(tof<T>(g0[e]), wk[e], gdot);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gdot = fmaf(tof<T>(g1[e]), wk[8 + e], gdot);
-    }
+    for (int kh = 0; kh < 2; ++kh) gdot = dot8(a[kh], *(const frag*)(wg + ks * 32 + 8 * (2 * kh + hl)), gdot);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -178,42 +214,39 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
     }
   }
 
-  // ---- row scale (x^ not yet normalised: sqrt(D) / |x|), rotary on q and k, q in log2 units
-  const int slot_me = 32 * half + r32;                  // this lane's band slot (token of tiles 0..3)
-  const int fr = f0 + fl;
-  const int64_t token = (int64_t)min(slot_me, NB - 1) * BT + min(fr, BT - 1);
-  float sc = 1.0f;
-  if (L.rowss) {
-    const float4* p = (const float4*)(L.rowss + token * kSsStride);
-    const float4 x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
-    const float ss = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w)) + ((x2.x + x2.y) + (x2.z + x2.w)) +
-                     ((x3.x + x3.y) + (x3.z + x3.w));
-    sc = L.rs_mul / fmaxf(sqrtf(ss), kNormEps);
-  }
+  // ---- gate; rotary on q and k, q in log2 units
   gdot += __shfl_xor(gdot, 32, 64);
   const float gate = sigmoidf_(gdot * sc + L.gate_bias[h]);
   // q (tiles 0, 1) and k (tiles 2, 3): element v is feature 32 (j%2) + 8 (v/4) + 4 hl + v%4 of the token
   // slot_me; pairs (2p, 2p+1) are elements (4g, 4g+1), (4g+2, 4g+3)
   frag qf[4], kf[4];
+  const float4* rhi = rt + (8 + (slot_me >> 3)) * 16;   // angles of slot 8 a + b = those of 8 a plus b
+  const float4* rlo = rt + (slot_me & 7) * 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * (j & 1) + 8 * g4 + 4 * hl;
-      const float2 cs = *(const float2*)(L.cos + slot_me * 32 + (d >> 1));
-      const float2 sn = *(const float2*)(L.sin + slot_me * 32 + (d >> 1));
-      float x[4];
+      const int d = 32 * jj + 8 * g4 + 4 * hl;
+      const float4 hi = rhi[d >> 2], lo = rlo[d >> 2];
+      const float2 cs = make_float2(hi.x * lo.x - hi.y * lo.y, hi.z * lo.z - hi.w * lo.w);
+      const float2 sn = make_float2(hi.y * lo.x + hi.x * lo.y, hi.w * lo.z + hi.z * lo.w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = acc[j][4 * g4 + e] * sc;
-      float y[4];
-      y[0] = x[0] * cs.x - x[1] * sn.x;
-      y[1] = x[0] * sn.x + x[1] * cs.x;
-      y[2] = x[2] * cs.y - x[3] * sn.y;
-      y[3] = x[2] * sn.y + x[3] * cs.y;
-      const float m = j < 2 ? L.q_mul : 1.0f;
-      frag& dst = j < 2 ? qf[2 * (j & 1) + (g4 >> 1)] : kf[2 * (j & 1) + (g4 >> 1)];
+      for (int j = jj; j < 4; j += 2) {    // q tile jj, then k tile jj + 2
+        float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[4 * (g4 & 1) + e] = cvt<T>(y[e] * m);
+        for (int e = 0; e < 4; ++e) x[e] = acc[j][4 * g4 + e] * sc;
+        float y[4];
+        y[0] = x[0] * cs.x - x[1] * sn.x;
+        y[1] = x[0] * sn.x + x[1] * cs.x;
+        y[2] = x[2] * cs.y - x[3] * sn.y;
+        y[3] = x[2] * sn.y + x[3] * cs.y;
+        const float m = j < 2 ? L.q_mul : 1.0f;
+        frag& dst = j < 2 ? qf[2 * jj + (g4 >> 1)] : kf[2 * jj + (g4 >> 1)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * (g4 & 1) + e] = cvt<T>(y[e] * m);
+      }
+      // two groups' rotary rows at a time: their results are made before the next groups' reads
+      if (g4 & 1) asm volatile("" : "+v"(qf[2 * jj + (g4 >> 1)]), "+v"(kf[2 * jj + (g4 >> 1)]) :: "memory");
     }
   }
   // v (tiles 4, 5): lane = feature 32 (j-4) + r32, element v = token slot 32 half + 8 (v/4) + 4 hl + v%4:
@@ -223,7 +256,7 @@ __global__ __launch_bounds__(128 * FR, 4 / FR) void band_attn_kernel(BandLaunch 
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float s = L.rowss ? __shfl(sc, 8 * (v >> 2) + 4 * hl + (v & 3), 64) : 1.0f;
+      const float s = __shfl(sc, 8 * (v >> 2) + 4 * hl + (v & 3), 64);   // sc = 1 without statistics
       vf[j][v >> 3][v & 7] = cvt<T>(acc[4 + j][v] * s);
     }
 
@@ -334,9 +367,9 @@ bool band_attn_supported(int dtype, int NB, int heads, int dh, int D) {
 
 hipError_t launch_band_attn(const BandLaunch& L, hipStream_t stream) {
   if (!band_attn_supported(L.dtype, L.NB, L.heads, 64, L.D) || L.BT < 1) return hipErrorInvalidValue;
-  // two frames (four waves) per workgroup, two workgroups per compute unit: one's projection
-  // overlaps the other's attention (0.90 ms per forward at 1100 frames against 0.97 for four frames
-  // per workgroup, one per compute unit)
+  // two frames (four waves) per workgroup, three workgroups per compute unit: one's projection
+  // overlaps the others' attention and load waits (0.86 ms per forward at 1100 frames; a 3-stage ring
+  // with two workgroups per compute unit 0.94, four frames per workgroup 0.97, one frame 1.73)
   if (L.dtype == DT_F16) return launch_fr<f16, 2>(L, stream);
   return launch_fr<bf16, 2>(L, stream);
 }
