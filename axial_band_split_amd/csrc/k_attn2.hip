@@ -11,15 +11,18 @@
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16: a lane owns one query column and 16 of
 //     the 32 keys of a tile, so a query's max needs one exchange with the lane 32 apart; the S^T
 //     accumulators start at minus the running reference, so a probability is one exponential; a
-//     lane adds up the fp32 probabilities it holds (one vector add each: the matrix core, already
-//     the busier unit, would spend a quarter more products on a ones-row sum at dh = 64);
+//     lane adds up the probabilities it holds as rounded to 16 bits (the values the P.V product
+//     uses), two per packed dot instruction against ones with fp32 accumulation (the matrix core,
+//     already the busier unit, would spend a quarter more products on a ones-row sum at dh = 64);
 //   * the probabilities feed the P.V product straight from the S^T accumulators: the K rows of the
 //     S^T product are taken in a permuted order so that the 8 probabilities a lane holds for one
 //     16-key step belong to 8 consecutive keys, and the matching V^T operand is one 16-byte read;
-//   * the reference used for the exponentials is the first tile's max, raised only when a later
-//     tile's max exceeds it by more than 8 (log2 units); until then the accumulators need no
-//     rescaling.  Any reference value gives the same softmax, the bound keeps every exponential
-//     <= 2^8;
+//   * the reference used for the exponentials is the first tile's max.  A later tile's
+//     exponentials are taken against it without looking at the tile's max; only when a lane's sum
+//     of them passes 2^12 (so one of them passed 2^7) is the tile's max taken, and the reference
+//     raised when that max exceeds it by more than 8 (log2 units), the accumulators rescaled and
+//     the exponentials taken again.  Any reference value gives the same softmax; the bounds keep
+//     every exponential that reaches the products <= 2^12, far inside the 16-bit range;
 //   * rows of 128 bytes hold their 16-byte chunks XOR-permuted by (row >> 1) & 7, so the rows one
 //     fragment read touches spread over all LDS banks;
 //   * only the last key tile is masked (keys >= n), and the workgroup order keeps all query blocks of
@@ -55,6 +58,23 @@ __device__ __forceinline__ f32x16 mma32c(const bf16x8& a, const bf16x8& b, const
 
 constexpr float kNegBig = -1e30f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the reference max must move
+constexpr float kSumBound = 4096.0f;   // a lane's tile sum past this: the tile's max is taken
+
+// sum of the eight values plus c, fp32 accumulation (packed dot instructions against ones)
+__device__ __forceinline__ float dot8_ones(const f16x8& a, float c) {
+  typedef f16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_fdot2(h2{a[2 * i], a[2 * i + 1]}, one, c, false);
+  return c;
+}
+__device__ __forceinline__ float dot8_ones(const bf16x8& a, float c) {
+  typedef bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_fdot2_f32_bf16(b2{a[2 * i], a[2 * i + 1]}, one, c, false);
+  return c;
+}
 constexpr int kKeysPerTile = 64;   // 128 halves the waits per key but leaves 2 instead of 3 workgroups per CU (slower)
 
 // LDS rows of 128 bytes (8 chunks of 16): chunk c of row r sits in slot c ^ ((r >> 1) & 7), so any
@@ -186,43 +206,62 @@ __global__ __launch_bounds__(256, 2) void attn_time2_kernel(AttnLaunch L) {
           if (key >= n) s[r][v] = kNegBig;
         }
     }
-    float mx = kNegBig;
+    // probabilities against the current reference, rounded to T, and the lane's sum of the rounded
+    // values (the ones the P.V product uses; packed dot instructions against ones)
+    frag pf[2 * RT];
+    auto probs = [&]() -> float {
+      float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+      for (int t = 0; t < 2 * RT; ++t) {
+        const int r = t >> 1, hv = (t & 1) * 8;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[r][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // the first tile sets the reference exactly; later ones move it only past kLazy
-    if (kt == 0 || __any(mx > kLazy)) {
-      const float up = kt == 0 ? mx : fmaxf(mx, 0.f);
-      if (kt > 0) {
-        const float alpha = __builtin_amdgcn_exp2f(-up);
-#pragma unroll
-        for (int d = 0; d < DT; ++d) o[d] *= alpha;
-        lsum_p *= alpha;
+        for (int e = 0; e < 8; ++e) pf[t][e] = cvt<T>(__builtin_amdgcn_exp2f(s[r][hv + e]));
+        sum = dot8_ones(pf[t], sum);
       }
-      mref += up;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) negm[v] = -mref;
-#pragma unroll
-      for (int r = 0; r < RT; ++r) s[r] -= up;
+      return sum;
+    };
+    // tile 0 sets the reference to its max; a later tile keeps it unless a lane's sum passes
+    // kSumBound (then some probability passed kSumBound / 32): only then is the tile's max taken
+    // and the reference moved as below
+    float tsum = 0.f;
+    bool redo = kt == 0;
+    if (!redo) {
+      tsum = probs();
+      redo = __any(!(tsum <= kSumBound));
     }
+    if (redo) {
+      float mx = kNegBig;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[r][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // the first tile sets the reference exactly; later ones move it only past kLazy
+      if (kt == 0 || __any(mx > kLazy)) {
+        const float up = kt == 0 ? mx : fmaxf(mx, 0.f);
+        if (kt > 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-up);
+#pragma unroll
+          for (int d = 0; d < DT; ++d) o[d] *= alpha;
+          lsum_p *= alpha;
+        }
+        mref += up;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) negm[v] = -mref;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) s[r] -= up;
+      }
+      tsum = probs();
+    }
+    lsum_p += tsum;
 #pragma unroll
     for (int t = 0; t < 2 * RT; ++t) {
-      const int r = t >> 1, hv = (t & 1) * 8;
-      frag pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(s[r][hv + e]);
-        lsum_p += pe;
-        pf[e] = cvt<T>(pe);
-      }
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         // V^T row (head dim) d*32 + l32, keys 16t + 8g .. +7: one 16-byte chunk
         const int row = d * 32 + l32;
         const frag a = *(const frag*)(st + KBYTES + row * VROWB + (((2 * t + g) ^ swz8(row)) << 4));
-        mma32(o[d], a, pf);
+        mma32(o[d], a, pf[t]);
       }
     }
   }
