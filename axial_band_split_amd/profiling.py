@@ -32,6 +32,12 @@ CAL_BYTES = 64 * 1024 * 1024 * 4      # the calibration copy moves 256 MiB in ea
 
 def short_name(k: str) -> str:
     k = k.replace("mbr::(anonymous namespace)::", "")
+    # rocprofv3 prints gemm2_kernel<bf16, EPI_QKV, Cfg> (mangled ...gemm2_kernelIDF16bLi1E...) demangled
+    # with its first two template arguments garbled; every other instantiation arrives mangled
+    m = re.match(r"void gemm2_kernel<bool _Accum, int, E, Cfg<(\d+), (\d+), (\d+), (\d+)> >", k)
+    if m:
+        bm, wm, wn, ns = map(int, m.groups())
+        return f"gemm2_kernel<bf16,qkv,{bm}x{64 * wn}/{wm}x{wn}w/{ns}st>"
     m = re.match(r"_ZN3mbr12_GLOBAL__N_1(\d+)(\w+?)I(.*)E(E|Ev).*", k)
     if m:
         n = int(m.group(1))

@@ -55,7 +55,7 @@ def shape_of(w: synth.Workload, total_width: int, batch: int | None = None) -> S
 
 # rocprofv3 kernel-name patterns of each kernel class on the 16-bit path (the GEMM's epilogue id is
 # its second template argument)
-KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E|embed_kernel", "qkv": r"gemm2_kernelIDF16b?_?Li1E",
+KIND_REGEX = {"embed": r"gemm2_kernelIDF16b?_?Li0E|embed_kernel", "qkv": r"gemm2_kernelIDF16b?_?Li1E|gemm2_kernel<bool _Accum, int, E,",
               "ffn1": r"gemm2_kernelIDF16b?_?Li2E", "out_proj": r"gemm2_kernelIDF16b?_?Li3E",
               "mask_hidden": r"gemm2_kernelIDF16b?_?Li4E", "mask_glu": r"gemm2_kernelIDF16b?_?Li5E",
               "ffn2": r"gemm2_kernelIDF16b?_?Li7E", "attn_time": r"attn_time2", "attn_band": r"attn_band",
