@@ -32,8 +32,9 @@
 // Whole device passes (one 128-token block per compute unit) run every hidden chunk in
 // each block.  The tokens left after them would leave most compute units idle for a full block's
 // time, so they run in blocks that each take one group of hidden chunks (the out-projection is
-// repeated per group): each block writes its part of the feed-forward sum (plus x1 in group 0),
-// and a small kernel adds the parts, b_2, and applies the two norms.
+// repeated per group), placed after the passes' blocks in the same grid so that they start on the
+// compute units the last pass frees: each writes its part of the feed-forward sum (plus x1 in
+// group 0), and a small kernel adds the parts, b_2, and applies the two norms.
 #include <type_traits>
 
 #include "kcommon.h"
@@ -119,22 +120,21 @@ struct BlockCfg {
 };
 
 template <typename T, typename C, bool ALL_CHUNKS>
-__global__ __launch_bounds__(C::THREADS, 2) void block_kernel(BlockLaunch L) {
+__device__ __forceinline__ void block_body(const BlockLaunch& L, const int bid, float* b1s) {
   typedef typename Frag<T>::type frag;
   constexpr int D = C::D, I = C::I, NS = C::NS, DT = C::DT, NCH = C::NCH, KO = C::KO, NST = C::NST,
                 SB = C::SB, R = C::R, FF = C::FF, GS = C::GS, TH = C::THREADS;
   auto none = [](auto) {};
   extern __shared__ __attribute__((aligned(16))) char smem[];   // the weight ring
-  __shared__ __attribute__((aligned(16))) float b1s[FF];        // b_1, a separate LDS object
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qd = lane >> 4;
   // block = (token group, chunk group q); a wave owns 16 tokens of the group's 128 and runs the
   // hidden chunks [c0, c0 + n) (n even, at least 2).  With ALL_CHUNKS (the whole passes) the
   // block runs every chunk and the trip counts are compile-time constants.
   const int groups = ALL_CHUNKS ? 1 : L.groups;
-  const int q = ALL_CHUNKS ? 0 : blockIdx.x % groups;
+  const int q = ALL_CHUNKS ? 0 : bid % groups;
   const int n = ALL_CHUNKS ? NCH : NCH / groups, c0 = q * n;
-  const int64_t token = (ALL_CHUNKS ? 0 : L.tok0) + (int64_t)(blockIdx.x / groups) * 128 + w * 16 + (lane & 15);
+  const int64_t token = (ALL_CHUNKS ? 0 : L.tok0) + (int64_t)(bid / groups) * 128 + w * 16 + (lane & 15);
   const bool valid = token < L.tokens;
   // lanes past the last token read the last token's row and store nothing (a token's lanes only
   // ever combine with each other)
@@ -388,6 +388,15 @@ __global__ __launch_bounds__(C::THREADS, 2) void block_kernel(BlockLaunch L) {
   }
 }
 
+// The whole device passes' blocks first, then the tail's (token group, chunk group) blocks, which
+// start on the compute units the last pass frees.
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 2) void block_kernel(BlockLaunch L) {
+  __shared__ __attribute__((aligned(16))) float b1s[C::FF];   // b_1, a separate LDS object
+  if ((int)blockIdx.x < L.main_blocks) block_body<T, C, true>(L, blockIdx.x, b1s);
+  else block_body<T, C, false>(L, blockIdx.x - L.main_blocks, b1s);
+}
+
 // x2 = b_2 + the chunk groups' parts (group 0 holds x1), then the epilogue of block_kernel:
 // x3 = RMSNorm_out(x2) -> X, XH = x3 normalised (or x3).  One wave per token, lane l holding
 // columns 2l, 2l + 1 of each 128-column slice.
@@ -452,27 +461,21 @@ template <typename T, typename C>
 hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
   static_assert(C::NCH % 24 == 0, "every group count splits the hidden chunks into even runs");
   if (L0.ncu < 1 || L0.tokens < 1) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C, true>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)block_kernel<T, C, false>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
   const int64_t pass = (int64_t)128 * L0.ncu, rest = L0.tokens % pass;
   BlockLaunch L = L0;
-  if (L0.tokens >= pass) {   // whole passes: 128 tokens and every hidden chunk to a block
-    L.tok0 = 0;
-    L.groups = 1;
-    const BlockLaunch Lm = [&] { BlockLaunch m = L; m.tokens = (int32_t)(L0.tokens - rest); return m; }();
-    hipLaunchKernelGGL((block_kernel<T, C, true>), dim3((unsigned)(Lm.tokens / 128)), dim3(C::THREADS), C::LDS, stream, Lm);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (rest == 0) return hipSuccess;
+  // whole passes: 128 tokens and every hidden chunk to a block
+  L.main_blocks = (int32_t)((L0.tokens - rest) / 128);
+  // the tail: (token group, chunk group) blocks, partial sums reduced by block_reduce_kernel
   const int64_t tb = (rest + 127) / 128;
   L.tok0 = L0.tokens - rest;
-  L.groups = tail_groups(tb, L0.ncu);
+  L.groups = rest ? tail_groups(tb, L0.ncu) : 1;
   if (L.groups > 1 && (!L.part || (size_t)L.groups * rest * C::D * 4 > block_part_bytes(C::D, L0.tokens, L0.ncu)))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((block_kernel<T, C, false>), dim3((unsigned)(tb * L.groups)), dim3(C::THREADS), C::LDS, stream, L);
-  if ((e = hipGetLastError()) != hipSuccess || L.groups == 1) return e;
+  const int64_t blocks = L.main_blocks + tb * L.groups;
+  hipLaunchKernelGGL((block_kernel<T, C>), dim3((unsigned)blocks), dim3(C::THREADS), C::LDS, stream, L);
+  if ((e = hipGetLastError()) != hipSuccess || rest == 0 || L.groups == 1) return e;
   hipLaunchKernelGGL((block_reduce_kernel<T, C::D>), dim3((unsigned)((rest + 3) / 4)), dim3(256), 0, stream, L);
   return hipGetLastError();
 }

@@ -222,6 +222,7 @@ struct BlockLaunch {
   // set by launch_block for each of its launches
   int64_t tok0;             // first token of the launch
   int32_t groups;           // hidden-chunk groups per 128 tokens (1: a block runs every chunk)
+  int32_t main_blocks;      // blocks of whole device passes at the start of the grid
 };
 size_t block_part_bytes(int D, int64_t tokens, int ncu);
 bool block_supported(int dtype, int D, int I, int FF);
