@@ -657,7 +657,7 @@ int run_forward(mbr_core* c, const float* in, float* out, int batch, hipStream_t
     const TransformerW& tw = c->tw[t];
     const int axis = t & 1;
     if (axis == 1 && c->use_band) {
-      // the band axis: q, k, v of one head for four frames, rotary, attention over the bands and
+      // the band axis: q, k, v of one head for two frames, rotary, attention over the bands and
       // the gate, in one kernel (q, k, v stay on the chip)
       BandLaunch bd{};
       bd.dtype = dt;
