@@ -189,6 +189,11 @@ __global__ __launch_bounds__(128 * FR, BandCfg<FR>::kOcc) void band_attn_kernel(
   for (int ks = 0; ks < nk; ++ks) {
     if (ks) wait_vm<0>();                   // this wave's loads of step ks
     block_barrier();                        // everyone's; and every wave is done with step ks-1
+    // the gate weights of this step, read before the next stage's loads are issued: an LDS read
+    // after them that the compiler cannot tell apart from the ring would wait for those loads
+    frag gw[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) gw[kh] = *(const frag*)(wg + ks * 32 + 8 * (2 * kh + hl));
     if (ks + 1 < nk) issue(ks + 1);         // into the slot of step ks-1
     const char* st = smem + (ks % kNS) * kStage;
     frag a[2], b[2][6];
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(128 * FR, BandCfg<FR>::kOcc) void band_attn_kernel(
     }
     // gate: chunks hl and 2 + hl of this step for the lane's token, the A fragments
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) gdot = dot8(a[kh], *(const frag*)(wg + ks * 32 + 8 * (2 * kh + hl)), gdot);
+    for (int kh = 0; kh < 2; ++kh) gdot = dot8(a[kh], gw[kh], gdot);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
