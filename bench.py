@@ -56,30 +56,43 @@ def kind_flops(s: roofline.Shape, kind: str, w: synth.Workload) -> float:
     return f[kind]
 
 
-def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
-    """The oracle on a bounded sample: the band embedding, the time and band Transformers of the
-    first layers (up to three), the mask head and the average of one forward, each timed once; the
-    forward's time is embedding + depth x (mean layer) + stems x (mask head + average), since every
-    layer has the same shape and cost."""
+def cpu_baseline(w: synth.Workload, ws, x_io, flops: float) -> dict:
+    """The oracle on a bounded sample of the same workload.  Up to 6 TFLOP per forward (the 11 s
+    chunk at depth 6 is 4.5, about half a minute on the host's cores) the whole oracle forward is
+    timed once; a larger forward is estimated from its parts, each timed once: the band embedding,
+    the time and band Transformers of the first layers (up to three), the mask head and the average,
+    as embedding + depth x (mean layer) + stems x (mask head + average), since every layer has the
+    same shape and cost."""
     from oracle import model as M
 
     cfg = M.CoreConfig(w.sample_rate, w.n_fft, w.audio_channels, w.num_bands, w.dim, w.depth, w.heads,
                        w.dim_head, w.ff_mult, w.mask_hidden_mult, w.mask_depth, w.num_stems)
-    tables = cfg.tables()
-    wn = M.named(cfg, ws)
-    spec = M.read_input(x_io, w.audio_channels, w.io_layout)
-    layers = min(w.depth, 3)
-    t0 = time.perf_counter()
-    x = M.band_embed(spec, cfg, wn, tables)
-    t1 = time.perf_counter()
-    for i in range(layers):
-        x = M.time_transformer(x, cfg, wn, f"layer{i}.time.", chunk=1)
-        x = M.band_transformer(x, cfg, wn, f"layer{i}.band.", chunk=64)
-    t2 = time.perf_counter()
-    m = M.mask_head(x, cfg, wn, tables, 0)
-    M.average(m, tables)
-    t3 = time.perf_counter()
-    est = (t1 - t0) + w.depth * (t2 - t1) / layers + w.num_stems * (t3 - t2)
+    if flops <= 6e12:
+        t0 = time.perf_counter()
+        M.forward(x_io, cfg, ws, layout=w.io_layout)
+        t3 = time.perf_counter()
+        est = t3 - t0
+        sample = (f"one whole fp64 numpy oracle forward of {w.name} ({w.audio_seconds:g} s of audio, every layer "
+                  f"and the mask head), timed once: {est:.1f} s")
+    else:
+        tables = cfg.tables()
+        wn = M.named(cfg, ws)
+        spec = M.read_input(x_io, w.audio_channels, w.io_layout)
+        layers = min(w.depth, 3)
+        t0 = time.perf_counter()
+        x = M.band_embed(spec, cfg, wn, tables)
+        t1 = time.perf_counter()
+        for i in range(layers):
+            x = M.time_transformer(x, cfg, wn, f"layer{i}.time.", chunk=1)
+            x = M.band_transformer(x, cfg, wn, f"layer{i}.band.", chunk=64)
+        t2 = time.perf_counter()
+        m = M.mask_head(x, cfg, wn, tables, 0)
+        M.average(m, tables)
+        t3 = time.perf_counter()
+        est = (t1 - t0) + w.depth * (t2 - t1) / layers + w.num_stems * (t3 - t2)
+        sample = (f"fp64 numpy oracle on {w.name}: band embedding, {layers} of {w.depth} layers (time + band "
+                  f"Transformer), mask head and average of stem 0, each timed once ({t3 - t0:.1f} s); "
+                  f"forward estimated as embed + {w.depth} x mean layer + {w.num_stems} x mask head = {est:.1f} s")
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -93,10 +106,8 @@ def cpu_baseline(w: synth.Workload, ws, x_io) -> dict:
     except Exception:
         blas = None
     return {"value": w.audio_seconds / est, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle on {w.name}: band embedding, {layers} of {w.depth} layers (time + band "
-                       f"Transformer), mask head and average of stem 0, each timed once ({t3 - t0:.1f} s); "
-                       f"forward estimated as embed + {w.depth} x mean layer + {w.num_stems} x mask head = {est:.1f} s"),
-            "host_cpus": os.cpu_count(), "blas": blas, "blas_threads": threads, "seconds_sampled": t3 - t0}
+            "sample": sample, "host_cpus": os.cpu_count(), "blas": blas, "blas_threads": threads,
+            "seconds_sampled": t3 - t0}
 
 
 def separation(w: synth.Workload, ws, seconds: float, repeats: int) -> dict:
@@ -245,7 +256,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample) ...")
-        cpu = cpu_baseline(w, ws, x_np)
+        cpu = cpu_baseline(w, ws, x_np, fl["total"])
         log(f"[bench] cpu baseline: {cpu['value']:.4f} audio-s/s ({cpu['sample']})")
 
     line = {
