@@ -53,6 +53,8 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+constexpr int kMaxTailGroups = 32;   // chunk groups of the tail at most (block_part_bytes)
+
 // A run of N products whose A fragments come from LDS, software-pipelined by hand: with one wave
 // per SIMD the wave issues in order and every stall is exposed, so
 //   region 0:      reads of group 0 (GS fragments)
@@ -216,12 +218,16 @@ __device__ __forceinline__ void block_body(const BlockLaunch& L, const int bid, 
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) ob[0][ks] = *(const frag*)(orow + 32 * ks);
   load_x(std::integral_constant<int, 0>{});
-  // loads issued after stage st's weights when stage st begins (in issue order: the weights of
-  // stage 1, o of stage 0 and residual part 0 for st = 0; those plus stage 0's o, weights and part
-  // for st = 1; then the part after the weights of st, and stage st-1's o, weights and part)
+  // loads issued after stage st's weights when stage st begins.  Three stages (two in flight): the
+  // weights of stage 1, o of stage 0 and residual part 0 for st = 0; those plus stage 0's o,
+  // weights and part for st = 1; then the part after the weights of st, and stage st-1's o, weights
+  // and part.  Two stages (one in flight): o of stage 0 and part 0 for st = 0; then the part issued
+  // after the weights of st.
+  static_assert(NS == 2 || NS == 3, "ring depth");
   auto wait_outproj = [&](auto st_) {
     constexpr int st = decltype(st_)::value;
-    constexpr int N = st == 0 ? R + 2 + XP : st == 1 ? R + 4 + 2 * XP : R + 2 + 2 * XP;
+    constexpr int N = NS == 3 ? (st == 0 ? R + 2 + XP : st == 1 ? R + 4 + 2 * XP : R + 2 + 2 * XP)
+                              : (st == 0 ? 2 + XP : XP);
     static_assert(N < 64, "vmcnt range");
     wait_vm<N>();
     block_barrier();
@@ -450,16 +456,17 @@ __global__ __launch_bounds__(256) void block_reduce_kernel(BlockLaunch L) {
 }
 
 // chunk groups per 128-token group of the tail: the most that keep the tail within one device pass
-int tail_groups(int64_t tail_blocks, int ncu) {
+// and split the nch hidden chunks into even runs (a block's loop takes its chunks two at a time)
+int tail_groups(int64_t tail_blocks, int ncu, int nch) {
   int g = 1;
-  for (int cand : {2, 3, 4, 6, 8, 12, 24})
-    if (tail_blocks * cand <= ncu) g = cand;
+  for (int cand = 2; cand <= kMaxTailGroups; ++cand)
+    if (nch % cand == 0 && (nch / cand) % 2 == 0 && tail_blocks * cand <= ncu) g = cand;
   return g;
 }
 
 template <typename T, typename C>
 hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
-  static_assert(C::NCH % 24 == 0, "every group count splits the hidden chunks into even runs");
+  static_assert(C::NCH % 2 == 0, "the hidden chunks go two at a time");
   if (L0.ncu < 1 || L0.tokens < 1) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)block_kernel<T, C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
@@ -470,7 +477,7 @@ hipError_t launch_t(const BlockLaunch& L0, hipStream_t stream) {
   // the tail: (token group, chunk group) blocks, partial sums reduced by block_reduce_kernel
   const int64_t tb = (rest + 127) / 128;
   L.tok0 = L0.tokens - rest;
-  L.groups = rest ? tail_groups(tb, L0.ncu) : 1;
+  L.groups = rest ? tail_groups(tb, L0.ncu, C::NCH) : 1;
   if (L.groups > 1 && (!L.part || (size_t)L.groups * rest * C::D * 4 > block_part_bytes(C::D, L0.tokens, L0.ncu)))
     return hipErrorInvalidValue;
   const int64_t blocks = L.main_blocks + tb * L.groups;
@@ -485,20 +492,19 @@ hipError_t launch_dt(const BlockLaunch& L, hipStream_t stream) {
   // LDS reads in groups of 3 fragments, 4 vector instructions after each feed-forward product (group
   // sizes 2, 3, 4 and 2, 4, 8 vector instructions time within 1%; 6 fragments about 1.5% slower)
   if (L.D == 384 && L.I == 512) return launch_t<T, BlockCfg<T, 384, 512, 3, 3, 4>>(L, stream);
+  // D = 512: two stages of 64 KB (three would take 192 KB of LDS), read groups of 2
+  if (L.D == 512 && L.I == 512) return launch_t<T, BlockCfg<T, 512, 512, 2, 2, 4>>(L, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// D = 512 needs more than the 256 registers of a wave that shares its SIMD (residual 128, normalised
-// operand 64, plus the hidden tiles and fragment buffers) and a 192 KB ring of three stages; that
-// width keeps the separate products.
 bool block_supported(int dtype, int D, int I, int FF) {
-  return dtype != DT_F32 && FF == 4 * D && I == 512 && D == 384;
+  return dtype != DT_F32 && FF == 4 * D && I == 512 && (D == 384 || D == 512);
 }
 
 size_t block_part_bytes(int D, int64_t tokens, int ncu) {
-  const int64_t tail = std::min<int64_t>((int64_t)128 * ncu, 24 * ((tokens + 127) / 128 * 128));
+  const int64_t tail = std::min<int64_t>((int64_t)128 * ncu, kMaxTailGroups * ((tokens + 127) / 128 * 128));
   return (size_t)tail * D * 4;
 }
 

@@ -162,7 +162,7 @@ int mbr_core_create(const mbr_config* cfg, const void* const* weights, int n_wei
  * Enqueued on `stream` (0 = the null stream); returns without waiting.  No allocation, no host
  * synchronisation and no atomics: the same input at the same batch size gives bitwise the same
  * masks.  Across batch sizes a chunk's masks agree to rounding, not bitwise: on the 16-bit path
- * with dim 384 the tokens after the last whole device pass sum their feed-forward in another fp32
+ * with dim 384 or 512 the tokens after the last whole device pass sum their feed-forward in another fp32
  * order, and which tokens those are depends on the batch.  The core's workspace serves one forward
  * at a time: calls on one core must be ordered (one stream, or streams joined by events), never
  * concurrent.  The caller keeps both buffers alive until the stream has passed this work.  The

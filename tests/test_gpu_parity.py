@@ -142,13 +142,15 @@ def test_fp32_stage_taps_match_oracle():
     assert rel_l2(y, ref) < 1e-5
 
 
+@pytest.mark.parametrize("base", ["t256_fp16", "heavy_b4_d512_bf16"])
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
-def test_half_precision_block_path_stage_taps(dtype):
-    """The 16-bit path of the vocals architecture (dim 384, 8 x 64 heads), where each Transformer's
-    out-projection, feed-forward and norms run as one kernel: x after every Transformer of a
-    two-layer core at 40 frames (2400 tokens, a ragged last group of 128) against the oracle's."""
-    w = synth.WORKLOADS["t256_fp16"].replace(frames=40, depth=2, dtype=dtype)
-    say(f"[taps] dim 384 {synth.DTYPE_NAMES[dtype]}, depth 2, T=40")
+def test_half_precision_block_path_stage_taps(dtype, base):
+    """The 16-bit path of the vocals architecture (dim 384, 8 x 64 heads) and of the heavy one (dim
+    512, the fused kernel's two-stage ring), where each Transformer's out-projection, feed-forward and
+    norms run as one kernel: x after every Transformer of a two-layer core at 40 frames (2400 tokens,
+    a ragged last group of 128) against the oracle's."""
+    w = synth.WORKLOADS[base].replace(frames=40, batch=1, depth=2, dtype=dtype)
+    say(f"[taps] dim {w.dim} {synth.DTYPE_NAMES[dtype]}, depth 2, T=40")
     cfg, ws = build(w, std=0.05, gamma_std=0.3)
     x = synth.draw_input(w)
     core = binding.Core(cfg, ws)
@@ -314,7 +316,10 @@ def test_heavy_full_size_against_oracle():
     """The heavy configuration at full size (4 chunks of 1100 frames, dim 512, depth 12, bf16, the
     launch configuration the benchmark times): finite; chunk 2 of the batch-4 call against the
     oracle's forward of that chunk (globally, per band and per 128-frame block, at the bf16 bar);
-    and each chunk's masks bitwise those of a batch-1 call on it (chunks never interact)."""
+    and against a batch-1 call on it.  Not bitwise: part of chunk 2's last band falls in the fused
+    kernel's chunk-group tail at batch 4 (tokens 262144 on) and not at batch 1, and the tail sums the
+    feed-forward in another fp32 order; the bf16 roundings this flips grow over the 24 Transformers
+    to about the size of the error against the oracle, so that bar is the bf16 one."""
     w = synth.WORKLOADS["heavy_b4_d512_bf16"]
     say("[heavy] full size, batch 4: chunk 2 against the oracle and a batch-1 call")
     cfg, ws = build(w)
@@ -325,8 +330,10 @@ def test_heavy_full_size_against_oracle():
     y1 = core.forward(xd[2:3].contiguous())
     torch.cuda.synchronize()
     assert torch.isfinite(y4).all()
-    assert torch.equal(y4[2:3], y1)
     y = y4[2:3].cpu().numpy()
+    e1 = rel_l2(y, y1.cpu().numpy().astype(np.float64))
+    say(f"[heavy] chunk 2: rel L2 vs a batch-1 call = {e1:.2e}")
+    assert e1 <= TOL[w.dtype]
     core.close()
     say("[heavy] oracle forward of chunk 2 (fp64 on the host)")
     ref = M.forward(x[2:3], ocfg(w), ws)
@@ -397,11 +404,12 @@ def test_frame_counts_off_the_presets(frames):
     assert err <= TOL[w.dtype]
 
 
-def _tail_groups(tokens: int, ncu: int = 256) -> int:
+def _tail_groups(tokens: int, ncu: int = 256, nch: int = 48) -> int:
     """Hidden-chunk groups the fused post-attention kernel gives the tokens after its whole device
-    passes of 128 * ncu (the most of 2, 3, 4, 6, 8, 12, 24 that keep them within one pass)."""
+    passes of 128 * ncu: the most, up to 32, that keep them within one pass and split the nch hidden
+    chunks of 32 into even runs (2, 3, 4, 6, 8, 12, 24 at dim 384; 2, 4, 8, 16, 32 at dim 512)."""
     blocks = -(-(tokens % (128 * ncu)) // 128)
-    return max([1] + [g for g in (2, 3, 4, 6, 8, 12, 24) if blocks * g <= ncu])
+    return max([1] + [g for g in range(2, 33) if nch % g == 0 and (nch // g) % 2 == 0 and blocks * g <= ncu])
 
 
 @pytest.mark.parametrize("frames,batch,groups", [(32, 1, 12), (32, 2, 8), (40, 2, 6), (96, 1, 4), (40, 4, 3),
@@ -423,6 +431,28 @@ def test_fused_kernel_tail_in_every_group_count(frames, batch, groups):
     core.close()
     err = rel_l2(y, M.forward(x, ocfg(w), ws))
     say(f"[tail] T={frames} B={batch}: rel L2 = {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("frames,batch,groups", [(16, 1, 32), (32, 1, 16), (64, 1, 8), (96, 1, 4), (96, 2, 2),
+                                                 (96, 4, 1)])
+def test_fused_kernel_tail_at_dim_512(frames, batch, groups):
+    """The heavy architecture (dim 512, bf16, one layer) on the fused kernel's two-stage ring, at
+    token counts whose tail runs in 32, 16, 8, 4, 2 and 1 hidden-chunk groups (on 256 compute
+    units), against the oracle."""
+    w = synth.WORKLOADS["heavy_b4_d512_bf16"].replace(frames=frames, batch=batch, depth=1)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    got_groups = _tail_groups(w.num_bands * frames * batch, ncu, nch=4 * w.dim // 32)
+    say(f"[tail512] T={frames} B={batch}: {got_groups} chunk groups on {ncu} compute units")
+    if ncu == 256:
+        assert got_groups == groups
+    cfg, ws = build(w, max_batch=batch)
+    x = synth.draw_input(w)
+    core = binding.Core(cfg, ws)
+    y = gpu_forward(core, x)
+    core.close()
+    err = rel_l2(y, M.forward(x, ocfg(w), ws))
+    say(f"[tail512] T={frames} B={batch}: rel L2 = {err:.3e}")
     assert err <= TOL[w.dtype]
 
 
