@@ -159,16 +159,23 @@ __device__ __forceinline__ void block_body(const BlockLaunch& L, const int bid, 
     for (int r = 0; r < R; ++r) buffer_dma16(srs, tid * 16, g + r * 16 * TH, l + r * 16 * TH);
   };
   // step i's stage is complete once at most (stages issued after it) * R loads are outstanding (the
-  // attention-output loads issued in between only make this wait longer than needed).  The next
-  // stage is requested once this one's LDS reads are all issued: its slot was last read in the
-  // previous step, which every wave finished before the barrier.
+  // attention-output loads issued in between only make this wait longer than needed).  With three
+  // stages the stage two ahead is requested once this step's LDS reads are all issued; with two,
+  // the next stage is requested right after the barrier, so that it has a whole step to arrive.
+  // Either way its slot was last read in the previous step, which every wave finished before the
+  // barrier.
   auto stage_begin = [&](int i) {
     if (i + NS - 2 < nsteps) wait_vm<(NS - 2) * R>();
     else wait_vm<0>();
     block_barrier();
+    if constexpr (NS == 2) {
+      if (i + 1 < nsteps) issue(i + 1);
+    }
   };
   auto stage_end = [&](int i) {
-    if (i + NS - 1 < nsteps) issue(i + NS - 1);
+    if constexpr (NS != 2) {
+      if (i + NS - 1 < nsteps) issue(i + NS - 1);
+    }
   };
 
 #pragma unroll
@@ -221,16 +228,16 @@ __device__ __forceinline__ void block_body(const BlockLaunch& L, const int bid, 
   // loads issued after stage st's weights when stage st begins.  Three stages (two in flight): the
   // weights of stage 1, o of stage 0 and residual part 0 for st = 0; those plus stage 0's o,
   // weights and part for st = 1; then the part after the weights of st, and stage st-1's o, weights
-  // and part.  Two stages (one in flight): o of stage 0 and part 0 for st = 0; then the part issued
-  // after the weights of st.
+  // and part.  Two stages (one in flight, the next requested right after the barrier): the o and the
+  // residual part of the stage, issued after its weights.
   static_assert(NS == 2 || NS == 3, "ring depth");
   auto wait_outproj = [&](auto st_) {
     constexpr int st = decltype(st_)::value;
-    constexpr int N = NS == 3 ? (st == 0 ? R + 2 + XP : st == 1 ? R + 4 + 2 * XP : R + 2 + 2 * XP)
-                              : (st == 0 ? 2 + XP : XP);
+    constexpr int N = NS == 3 ? (st == 0 ? R + 2 + XP : st == 1 ? R + 4 + 2 * XP : R + 2 + 2 * XP) : 2 + XP;
     static_assert(N < 64, "vmcnt range");
     wait_vm<N>();
     block_barrier();
+    if constexpr (NS == 2) issue(st + 1);
   };
   static_for<KO>([&](auto st_) {
     constexpr int st = decltype(st_)::value;
