@@ -1,0 +1,123 @@
+"""Host logic of bench.py and of the counter records it reads (no GPU needed): the one-GPU refusal,
+the calibrated traffic arithmetic, the staleness check of a traffic record, and the committed bench
+lines' own arithmetic against the FLOP model."""
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from axial_band_split_amd import binding, profiling, roofline, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""          # no JSON line for a configuration that was not measured
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, c, v in rows:
+            wr.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_traffic_record_arithmetic(tmp_path):
+    """Two instantiations of one kernel class count as one launch of both (the mean per dispatch of
+    each, summed); other kernels are ignored; each counter is scaled by what it reads for a copy of
+    known size."""
+    a, b, other = "void mbr::block_kernel<A>(x)", "void mbr::block_reduce_kernel<A>(y)", "void mbr::attn_time2_kernel<A>(z)"
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, [(a, "FETCH_SIZE", 1000), (a, "FETCH_SIZE", 3000), (b, "FETCH_SIZE", 10),
+                         (other, "FETCH_SIZE", 1e9), (a, "WRITE_SIZE", 1e9)])
+    _counter_csv(write, [(a, "WRITE_SIZE", 400), (b, "WRITE_SIZE", 6), (b, "WRITE_SIZE", 2),
+                         (other, "WRITE_SIZE", 1e9)])
+    cal_f = tmp_path / "cal_fetch.csv"
+    cal_w = tmp_path / "cal_write.csv"
+    # the copy reads twice and writes once what it moves (in KiB): factors 1/2 and 1
+    kib = profiling.CAL_BYTES / 1024
+    _counter_csv(cal_f, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * kib), (other, "FETCH_SIZE", 9 * kib)])
+    _counter_csv(cal_w, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)])
+    rec = profiling.traffic_record(str(fetch), str(write), str(cal_f), str(cal_w), roofline.KIND_REGEX["block"],
+                                   "cmd", sources=profiling.KIND_SOURCES["block"])
+    assert rec["fetch_kib_per_dispatch"] == 2000 + 10
+    assert rec["write_kib_per_dispatch"] == 400 + 4
+    assert rec["fetch_factor"] == pytest.approx(0.5) and rec["write_factor"] == pytest.approx(1.0)
+    assert rec["bytes_per_launch"] == pytest.approx((2010 * 0.5 + 404) * 1024)
+    assert rec["source_sha"] == profiling.source_hash(profiling.KIND_SOURCES["block"])
+
+
+def test_traffic_record_is_dropped_when_stale(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_for("wl", "block") is None                      # no record
+    os.makedirs(tmp_path / "profiles")
+    files = list(profiling.KIND_SOURCES["block"])
+    rec = {"kernel_regex": roofline.KIND_REGEX["block"], "source_files": files,
+           "source_sha": profiling.source_hash(files), "bytes_per_launch": 123.0}
+    path = tmp_path / "profiles" / "traffic_wl.json"
+    path.write_text(json.dumps(rec))
+    assert bench.traffic_for("wl", "block") == 123.0
+    assert bench.traffic_for("wl", "qkv") is None                        # another kernel class
+    path.write_text(json.dumps(dict(rec, source_sha="0" * 16)))
+    assert bench.traffic_for("wl", "block") is None                      # sources changed since
+    path.write_text(json.dumps(dict(rec, kernel_regex="block_kernel")))
+    assert bench.traffic_for("wl", "block") is None                      # other kernels counted
+
+
+def test_source_hash_covers_only_the_named_files():
+    files = profiling.KIND_SOURCES["block"]
+    assert profiling.source_hash(files) == profiling.source_hash(tuple(reversed(files)))
+    assert profiling.source_hash(files) != profiling.source_hash(files[:-1])
+    assert profiling.source_hash(files) != profiling.source_hash()
+
+
+RECORDS = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
+
+
+@pytest.mark.parametrize("path", RECORDS, ids=[os.path.basename(p) for p in RECORDS])
+def test_committed_bench_lines_are_self_consistent(path):
+    """Each committed bench line: the contract's fields, the throughput from its own step time, the
+    dominant kernel's FLOP count from the FLOP model at that workload, its rate and fraction of the
+    peak from its own launch time, and its traffic equal to the committed counter record's."""
+    line = json.loads(open(path).read().strip().splitlines()[-1])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in line, k
+    assert line["n_gpus"] == 1 and line["higher_is_better"] is True and line["data"] == "synthetic"
+    w = synth.WORKLOADS[line["config"]["workload"]]
+    assert line["dtype"] == synth.DTYPE_NAMES[w.dtype]
+    assert line["config"]["audio_seconds_per_step"] == pytest.approx(w.audio_seconds)
+    assert line["value"] == pytest.approx(w.audio_seconds / (line["ms_per_step"] * 1e-3), rel=1e-9)
+
+    roof = line["roofline"]
+    kind = roof["kernel"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+    assert roof["peak"] == roofline.PEAK_MFMA_TFLOPS[w.dtype]
+    _, total_width, _ = binding.mbr_core_table_sizes(binding.config(w))
+    s = roofline.shape_of(w, total_width)
+    assert roof["flops_per_launch"] == pytest.approx(bench.kind_flops(s, kind, w), rel=1e-12)
+    assert roof["avg_launch_ms"] == line["kernels"][kind]["avg_launch_ms"]
+    assert roof["achieved"] == pytest.approx(roof["flops_per_launch"] / (roof["avg_launch_ms"] * 1e-3) / 1e12, rel=1e-9)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-12)
+    assert kind == max(line["kernels"], key=lambda k: line["kernels"][k]["ms_per_step"])
+    if roof["traffic"] is not None:
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")))
+        assert rec["kernel_regex"] == roofline.KIND_REGEX[kind]
+        # a line may predate a re-take of the record on the same sources: two takes of the
+        # counters differ by about 1e-5
+        assert roof["traffic"] == pytest.approx(rec["bytes_per_launch"], rel=1e-3)
+
+    cpu = line["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["unit"] == line["unit"] and cpu["cores"] >= 1 and cpu["sample"]
