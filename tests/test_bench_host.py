@@ -5,6 +5,7 @@ import csv
 import glob
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -121,3 +122,27 @@ def test_committed_bench_lines_are_self_consistent(path):
 
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == line["unit"] and cpu["cores"] >= 1 and cpu["sample"]
+
+
+TRAFFIC = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")))
+
+
+@pytest.mark.parametrize("path", TRAFFIC, ids=[os.path.basename(p) for p in TRAFFIC])
+def test_committed_traffic_records_are_self_consistent(path):
+    """A traffic record's bytes follow from its own counter means and calibration factors, the
+    factors from the calibration copy it names, and its command runs files of this repository."""
+    rec = json.load(open(path))
+    want = (rec["fetch_kib_per_dispatch"] * rec["fetch_factor"] + rec["write_kib_per_dispatch"] * rec["write_factor"]) * 1024
+    assert rec["bytes_per_launch"] == pytest.approx(want, rel=1e-12)
+    m = re.match(r"device copy of (\d+) bytes: FETCH_SIZE (\d+) KiB, WRITE_SIZE (\d+) KiB", rec["calibration"])
+    assert m, rec["calibration"]
+    moved, f_kib, w_kib = (int(g) for g in m.groups())
+    assert moved == profiling.CAL_BYTES
+    # the calibration line prints whole KiB (about 4e-6 of the copy's counter reading)
+    assert rec["fetch_factor"] == pytest.approx(moved / (f_kib * 1024), rel=1e-5)
+    assert rec["write_factor"] == pytest.approx(moved / (w_kib * 1024), rel=1e-5)
+    assert rec["kernel_regex"] in roofline.KIND_REGEX.values()
+    assert rec["source_files"] and all(os.path.exists(os.path.join(ROOT, "axial_band_split_amd", "csrc", f))
+                                       for f in rec["source_files"])
+    for f in re.findall(r"\$R/(\S+\.py)", rec["command"]):
+        assert os.path.exists(os.path.join(ROOT, f)), f
