@@ -146,3 +146,20 @@ def test_committed_traffic_records_are_self_consistent(path):
                                        for f in rec["source_files"])
     for f in re.findall(r"\$R/(\S+\.py)", rec["command"]):
         assert os.path.exists(os.path.join(ROOT, f)), f
+
+
+SUMMARIES = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+
+
+@pytest.mark.parametrize("path", SUMMARIES, ids=[os.path.basename(p) for p in SUMMARIES])
+def test_profile_summaries_name_a_command_of_committed_files(path):
+    """Every rocprofv3 summary is short text that gives the command it came from, and that command
+    runs files of this repository."""
+    text = open(path).read()
+    assert len(text) < 16 * 1024
+    cmd = re.search(r"^Command[^:]*: (.+)$", text, re.M)
+    assert cmd, "no command line"
+    scripts = re.findall(r"python3 (?:\$R/)?(\S+?\.py)\b", cmd.group(1))   # $R or relative to the root
+    assert scripts, cmd.group(1)
+    for f in scripts:
+        assert os.path.exists(os.path.join(ROOT, f)), f
