@@ -61,6 +61,23 @@ def test_vectorised_matches_brute_force(kw, B, T, seed):
     assert np.abs(y - yb).max() <= 1e-12 * max(1.0, np.abs(yb).max())
 
 
+def test_stems_match_brute_force_stem_by_stem():
+    """Several mask heads on one trunk: the oracle's stem axis (after the batch axis) holds each
+    stem's masks in order, each from that stem's own weights ([P1] "Model family and the three
+    local checkpoints": the two-stem model shares the trunk and has one mask head per stem)."""
+    cfg = tiny(num_stems=3, depth=1)
+    ws = synth.draw_weights(M.inventory(cfg), synth.F32, seed=11, std=0.4, gamma_std=0.3)
+    x = np.random.default_rng(12).standard_normal((2, (cfg.n_fft // 2 + 1) * 2, 3, 2))
+    y = M.forward(x, cfg, ws)
+    assert y.shape == (2, 3, (cfg.n_fft // 2 + 1) * 2, 3, 2)
+    w = M.named(cfg, ws)
+    for s in range(3):
+        yb = np.array(brute.forward(x, cfg.sample_rate, cfg.n_fft, 2, cfg.num_bands, cfg.dim, cfg.depth, cfg.heads,
+                                    cfg.dim_head, cfg.mask_depth, w, stem=s))
+        assert np.abs(y[:, s] - yb).max() <= 1e-12 * max(1.0, np.abs(yb).max())
+    assert np.abs(y[:, 0] - y[:, 1]).max() > 1e-3          # the heads differ, so the order is seen
+
+
 def test_brute_force_catches_a_planted_mistake():
     """A mistake planted in the oracle (a transposed projection) must fail the comparison."""
     cfg = tiny()
