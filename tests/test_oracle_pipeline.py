@@ -148,3 +148,28 @@ def test_half_chunk_separation_with_unit_masks_returns_the_track(L):
     out = P.separate(wave, unit_core, n_fft, hop, chunk, stems=1, stride=chunk // 2)
     assert out.shape == (1, 2, L)
     assert np.allclose(out[0], wave, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("stride", [None, 1024])
+def test_separation_with_constant_masks_scales_each_stem_and_channel(stride):
+    """Real masks c[stem, channel] (pair p = f * S + s): the iSTFT is linear and the fades sum to
+    one, so stem k's channel s comes back as c[k, s] times the track's channel s; masks that were
+    ignored, or stems or channels taken in the wrong order, fail this."""
+    n_fft, hop, chunk, L = 256, 64, 2048, 7000
+    S = 2
+    wave = np.random.default_rng(8).standard_normal((S, L))
+    c = np.array([[0.25, -1.5], [2.0, 0.5], [-0.75, 3.0]])          # [stems, channels]
+
+    def const_core(spec):
+        FS = spec.shape[1]
+        m = np.zeros((3,) + spec.shape[1:])
+        for k in range(3):
+            for s in range(S):
+                m[k, s:FS:S, :, 0] = c[k, s]
+        return m
+
+    out = P.separate(wave, const_core, n_fft, hop, chunk, stems=3, stride=stride)
+    assert out.shape == (3, S, L)
+    for k in range(3):
+        for s in range(S):
+            assert np.allclose(out[k, s], c[k, s] * wave[s], rtol=0, atol=1e-9)
