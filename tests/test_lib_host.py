@@ -135,3 +135,42 @@ def test_bad_band_tables_are_refused(bins):
     with pytest.raises(binding.MbrError) as e:
         binding.mbr_core_weight_count(binding.config(w))
     assert e.value.code == -2
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C99 program that includes the header, takes the address of every function it declares
+    (so each must link) and calls the host queries: the boundary needs no C++ and no torch."""
+    names = _declared_functions()
+    w = synth.WORKLOADS["tiny_fp32"]
+    src = ["#include <stdio.h>", "#include <string.h>", '#include "mbr_core.h"',
+           "typedef void (*fn)(void);",
+           "static const fn all[] = {" + ", ".join(f"(fn){n}" for n in names) + "};",
+           "int main(void) {",
+           "  mbr_config bad; memset(&bad, 0, sizeof bad);",
+           "  int rc = mbr_core_weight_count(&bad);",
+           "  const char* msg = mbr_last_error();",
+           "  if (rc != MBR_E_CONFIG || strncmp(msg, \"invalid config\", 14) != 0) return 1;",
+           "  mbr_config c; memset(&c, 0, sizeof c);",
+           f"  c.sample_rate = {w.sample_rate}; c.n_fft = {w.n_fft}; c.audio_channels = {w.audio_channels};",
+           f"  c.num_bands = {w.num_bands}; c.dim = {w.dim}; c.depth = {w.depth}; c.heads = {w.heads};",
+           f"  c.dim_head = {w.dim_head}; c.ff_mult = {w.ff_mult}; c.mask_hidden_mult = {w.mask_hidden_mult};",
+           f"  c.mask_depth = {w.mask_depth}; c.num_stems = {w.num_stems}; c.max_batch = 1; c.frames = {w.frames};",
+           f"  c.dtype = {w.dtype}; c.io_layout = {w.io_layout}; c.band_bins = NULL;",
+           "  int n = mbr_core_weight_count(&c);",
+           "  if (n <= 0) return 2;",
+           "  printf(\"%d %d\\n\", n, (int)(sizeof all / sizeof all[0]));",
+           "  return 0;",
+           "}"]
+    (tmp_path / "abi.c").write_text("\n".join(src) + "\n")
+    libdir = os.path.dirname(binding.LIB_PATH)
+    exe = tmp_path / "abi"
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                         "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{os.path.dirname(HEADER)}",
+                         str(tmp_path / "abi.c"), "-o", str(exe), f"-L{libdir}", "-lmbr_core",
+                         f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr[-2000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    n, count = map(int, run.stdout.split())
+    assert n == binding.mbr_core_weight_count(binding.config(w))
+    assert count == len(names)
