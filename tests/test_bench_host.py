@@ -163,3 +163,16 @@ def test_profile_summaries_name_a_command_of_committed_files(path):
     assert scripts, cmd.group(1)
     for f in scripts:
         assert os.path.exists(os.path.join(ROOT, f)), f
+
+
+@pytest.mark.parametrize("path", TRAFFIC, ids=[os.path.basename(p) for p in TRAFFIC])
+def test_algorithmic_bytes_do_not_exceed_the_measured_traffic(path):
+    """The byte model counts every operand once, so a launch cannot move fewer HBM bytes than it
+    gives; a term counted twice or in the wrong width would show here as more than was measured."""
+    rec = json.load(open(path))
+    name = os.path.basename(path)[len("traffic_"):-len(".json")]
+    w = synth.WORKLOADS[name]
+    kind = next(k for k, v in roofline.KIND_REGEX.items() if v == rec["kernel_regex"])
+    _, total_width, _ = binding.mbr_core_table_sizes(binding.config(w))
+    algo = roofline.bytes_per_launch(roofline.shape_of(w, total_width))[kind]
+    assert 0.5 * rec["bytes_per_launch"] < algo <= rec["bytes_per_launch"]

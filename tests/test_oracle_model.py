@@ -43,6 +43,14 @@ def test_param_counts_match_printed():
     assert round(mask / 1e6) == v["mask_head_params_millions"]
 
 
+def test_fp32_weight_set_size_of_the_vocals_model():
+    """[P1] "Compute-bound or memory-bound?": the vocals model's fp32 weight set is 871 MiB."""
+    g = json.load(open(os.path.join(GOLDEN, "model_sizes.json")))["vocals"]
+    c = M.CoreConfig(44100, 2048, 2, 60, g["dim"], g["depth"], g["heads"], g["dim_head"], num_stems=g["num_stems"])
+    n = sum(int(np.prod(s)) for _, s, _ in M.inventory(c))
+    assert round(4 * n / 2 ** 20) == 871
+
+
 # ----------------------------------------------------------------------------- brute force
 
 @pytest.mark.parametrize("kw,B,T,seed", [
