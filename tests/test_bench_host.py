@@ -176,3 +176,14 @@ def test_algorithmic_bytes_do_not_exceed_the_measured_traffic(path):
     _, total_width, _ = binding.mbr_core_table_sizes(binding.config(w))
     algo = roofline.bytes_per_launch(roofline.shape_of(w, total_width))[kind]
     assert 0.5 * rec["bytes_per_launch"] < algo <= rec["bytes_per_launch"]
+
+
+def test_sweep_rows_follow_from_their_step_times():
+    """Each row of the committed sweep: audio seconds per step = B * T * hop / sample rate (hop 441
+    at 44.1 kHz, whatever the stem count), divided by the row's step time."""
+    rows = [ln.split("|")[1:-1] for ln in open(os.path.join(ROOT, "profiles", "sweep_chunk11s_fp16.md"))
+            if ln.startswith("| ") and not ln.startswith("| workload")]
+    assert len(rows) >= 8
+    for r in rows:
+        B, T, ms, rate = int(r[1]), int(r[2]), float(r[4]), float(r[5])
+        assert rate == pytest.approx(B * T * 441 / 44100 / (ms * 1e-3), rel=2e-3), r[0]
