@@ -187,3 +187,34 @@ def test_sweep_rows_follow_from_their_step_times():
     for r in rows:
         B, T, ms, rate = int(r[1]), int(r[2]), float(r[4]), float(r[5])
         assert rate == pytest.approx(B * T * 441 / 44100 / (ms * 1e-3), rel=2e-3), r[0]
+
+
+def _ignored(path: str, pattern: str) -> bool:
+    """tar-style exclusion: './p' anchors at the top, any other pattern matches at any depth."""
+    import fnmatch
+    parts = path.split("/")
+    if pattern.startswith("./"):
+        p = pattern[2:]
+        return any(fnmatch.fnmatch("/".join(parts[:i]), p) for i in range(1, len(parts) + 1))
+    return any(fnmatch.fnmatch("/".join(parts[i:j]), pattern)
+               for i in range(len(parts)) for j in range(i + 1, len(parts) + 1))
+
+
+def test_gpu_runs_receive_every_file_they_load():
+    """No pattern of the push's ignore list drops the library's sources, the oracle, the header,
+    the bench and its counter records, or a test that the GPU suite collects."""
+    ign = os.path.join(ROOT, ".gpurunignore")
+    patterns = [ln.strip() for ln in open(ign) if ln.strip() and not ln.startswith("#")]
+    files = subprocess.run(["git", "ls-files"], cwd=ROOT, capture_output=True, text=True).stdout.split()
+    if not files:
+        pytest.skip("not a git checkout")
+    host_only = {"tests/test_host_sanitized.py", "tests/host_tables_driver.cpp"}
+    needed = [f for f in files if f.split("/")[0] in ("axial_band_split_amd", "oracle", "include", "profiles", "tests")
+              or f in ("bench.py", "__graft_entry__.py")]
+    needed = [f for f in needed if f not in host_only and not f.endswith(".md")]
+    assert "profiles/traffic_chunk11s_fp16.json" in needed
+    for f in needed:
+        hit = [p for p in patterns if _ignored(f, p)]
+        assert not hit, (f, hit)
+    for f in host_only:
+        assert any(_ignored(f, p) for p in patterns), f
